@@ -1,0 +1,249 @@
+"""Benchmark of one compensated block-sparse decode step on one MI355X.
+
+Workload: a Llama-3.1-8B-shaped attention layer decoding with a 128K-token
+context and a 512-token budget (B=1, Hq=32, Hkv=8, d=128, 16-token blocks,
+r=4, bf16), synthetic seeded inputs.  A step is one ckv_decode_step call
+(score every block, select the top-k, attend exactly to the selected blocks
+with Mean compensation of the rest).  Steps rotate over `--layers` copies of
+the layer (distinct buffers), so each step reads its summaries from HBM, not
+from the last-level cache, as a model's layer loop would.
+
+Prints one JSON line.  `value` is microseconds per layer decode step (lower
+is better); the effective HBM rate over the algorithmic bytes is reported
+beside it, with the roofline of the step's kernels, full dense decode on the
+same GPU, and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs per layer decode step & effective HBM GB/s (% peak) at 128K ctx, 512 budget"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ("kernels.hip", "device.hpp", "internal.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "compensated_kv_selection_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(M: int, Hkv: int, d: int, r: int, k: int, bs: int, kv_bytes: int) -> dict:
+    """Bytes a decode step must move: every block's summary (mean key, mean
+    value, r grouped variances per KV head, one count per block) plus the
+    selected blocks' keys and values."""
+    summary = M * Hkv * (2 * d * kv_bytes + 4 * r) + 4 * M
+    selected = Hkv * k * bs * d * 2 * kv_bytes
+    return {"summary": summary, "selected_kv": selected, "total": summary + selected}
+
+
+def read_traffic(kernel_tag: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=16, help="distinct layer buffers the steps rotate over")
+    ap.add_argument("--workload", default="llama_128k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-steps", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode step shards by KV head or by sequence; see the design notes)",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from compensated_kv_selection_amd import compkv as C
+    from compensated_kv_selection_amd import workloads as W
+    from compensated_kv_selection_amd.tensors import to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev0 = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20)
+        x = torch.empty(n, dtype=torch.uint8, device=dev0).fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return 0
+
+    C.load_library()
+    t_gen = time.time()
+    w = W.make_preset(args.workload, seed=args.seed)
+    print(f"[bench] generated {args.workload} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    base = to_device(w, dev0)
+    dims = base.dims
+    budget = w.budget_tokens
+    L = int(w.seq_lens.max())
+    M = -(-L // w.block_size)
+    kv_bytes = 2 if w.dtype == "bf16" else 4
+    kk = min(M, budget // w.block_size)
+
+    # Layer copies (distinct buffers); summaries built per layer.
+    layers = []
+    for li in range(args.layers):
+        kc = base.k_cache if li == 0 else base.k_cache.clone()
+        vc = base.v_cache if li == 0 else base.v_cache.clone()
+        summ = C.allocate_summaries(dims, dev0)
+        layers.append((kc, vc, summ))
+    torch.cuda.synchronize()
+
+    # Prefill summary build over the whole context (timed, reported beside the step).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    build_ms = []
+    for li, (kc, vc, summ) in enumerate(layers):
+        ev[0].record()
+        C.build_summaries(dims, kc, vc, base.block_table, base.seq_lens, summ)
+        ev[1].record()
+        torch.cuda.synchronize()
+        build_ms.append(ev[0].elapsed_time(ev[1]))
+    build_us = float(np.median(build_ms[1:] if len(build_ms) > 1 else build_ms)) * 1e3
+
+    ws = C.allocate_workspace(C.workspace_bytes(dims, budget), dev0)
+    sel = torch.empty((dims.batch, dims.num_kv_heads, max(1, dims.kmax(budget))), dtype=torch.int32, device=dev0)
+    nsel = torch.empty((dims.batch, dims.num_kv_heads), dtype=torch.int32, device=dev0)
+    out = torch.empty((dims.batch, dims.num_q_heads, dims.head_dim), dtype=torch.float32, device=dev0)
+    lse = torch.empty((dims.batch, dims.num_q_heads), dtype=torch.float32, device=dev0)
+
+    def step(i):
+        kc, vc, summ = layers[i % len(layers)]
+        C.decode_step(dims, base.q, kc, vc, summ, base.block_table, base.seq_lens, budget, ws,
+                      selected=sel, num_selected=nsel, out=out, lse=lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step(args.warmup + i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    region_ms = starts[0].elapsed_time(ends[-1])
+    per_launch_us = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3
+    us_per_step = region_ms * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps: {us_per_step:.2f} us/step (events), "
+          f"median launch {np.median(per_launch_us):.2f} us, wall {wall_s * 1e6 / args.steps:.1f} us/step",
+          file=sys.stderr, flush=True)
+
+    ab = algorithmic_bytes(M, w.num_kv_heads, w.head_dim, w.r_groups, kk, w.block_size, kv_bytes)
+    avg_launch_us = float(per_launch_us.mean())
+    achieved = ab["total"] / (avg_launch_us * 1e-6) / 1e9
+    eff_gbps = ab["total"] / (us_per_step * 1e-6) / 1e9
+
+    dense = None
+    if not args.no_dense:
+        dws = C.allocate_workspace(C.dense_workspace_bytes(dims), dev0)
+        dout = torch.empty_like(out)
+        dlse = torch.empty_like(lse)
+
+        def dstep(i):
+            kc, vc, _ = layers[i % len(layers)]
+            C.dense_decode_attention(dims, base.q, kc, vc, base.block_table, base.seq_lens, dws,
+                                     out=dout, lse=dlse)
+
+        dn = max(10, args.steps // 4)
+        for i in range(5):
+            dstep(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(dn):
+            dstep(i)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_us = e0.elapsed_time(e1) * 1e3 / dn
+        dense_bytes = M * w.num_kv_heads * w.block_size * w.head_dim * 2 * kv_bytes
+        dense = {"us_per_step": round(dense_us, 2), "bytes": dense_bytes,
+                 "GBps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+                 "speedup_of_compkv": round(dense_us / us_per_step, 2)}
+
+    cpu = None
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+        from oracle import compkv_oracle as O
+        with threadpool_limits(limits=1):
+            q, k, v = O.sequence_arrays(w.q[0], w.k_tokens[0], w.v_tokens[0], w.dtype)
+            osumm = O.build_summaries(k, v, w.block_size, w.r_groups, w.dtype)
+            t0 = time.perf_counter()
+            for _ in range(args.cpu_steps):
+                O.decode_step(q, k, v, osumm, budget_tokens=budget, block_size=w.block_size, r=w.r_groups)
+            cpu_s = (time.perf_counter() - t0) / args.cpu_steps
+        cpu = {"value": round(cpu_s * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+               "sample": f"{args.cpu_steps} float64 numpy oracle decode steps of the same 128K-token "
+                         f"layer (summaries prebuilt, one BLAS thread), host CPU"}
+
+    src_hash = kernel_source_hash()
+    traffic = read_traffic("decode_step_" + args.workload, src_hash)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": "decode step (ckv_decode_step launches)",
+            "algorithmic_bytes_per_launch": ab["total"], "avg_launch_us": round(avg_launch_us, 3)}
+    line = {
+        "metric": METRIC, "value": round(us_per_step, 3), "unit": "us/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_per_step / 1e3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: decode step, batch {w.batch}, {L} tokens, Hq "
+                               f"{w.num_q_heads}, Hkv {w.num_kv_heads}, d {w.head_dim}, block "
+                               f"{w.block_size}, r {w.r_groups}, budget {budget} tokens ({kk} blocks), "
+                               f"{args.layers} rotating layer buffers",
+                   "global_batch": w.batch, "seq_len": L, "budget_tokens": budget},
+        "effective_GBps": round(eff_gbps, 1), "pct_hbm_peak": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes": ab, "roofline": roof, "dense": dense,
+        "summary_build": {"us": round(build_us, 1),
+                          "bytes": M * w.num_kv_heads * w.block_size * w.head_dim * 2 * kv_bytes
+                          + ab["summary"],
+                          "GBps": round((M * w.num_kv_heads * w.block_size * w.head_dim * 2 * kv_bytes
+                                         + ab["summary"]) / (build_us * 1e-6) / 1e9, 1)},
+        "cpu_baseline": cpu, "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

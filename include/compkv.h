@@ -1,0 +1,208 @@
+/*
+ * compkv.h - C ABI of libcompkv.so: compensation-aware block-sparse decode
+ * attention (CompKV) on AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of one attention layer, for a batch of sequences whose
+ * keys and values live in a paged cache on the GPU:
+ *
+ *   1. ckv_build_summaries: per block (= page) and KV head, the mean key,
+ *      the grouped key variance (r channel groups), the mean value and the
+ *      token count.  CompKV review (evolve.pub), "Summary" and the FAQ: the
+ *      method keeps mean key, grouped key variances (4 groups by default)
+ *      and mean value, 2d + r + 1 scalars per block, updated as tokens enter
+ *      the cache.
+ *   2. ckv_score_select: score every block from its summary with the
+ *      practical residual criterion - a second-order attention-mass estimate
+ *      times the estimated within-block logit variance - and keep the top-k
+ *      blocks under a token budget.  CompKV abstract (shd-paper.top listing):
+ *      the residual left by block-level mean compensation is governed by
+ *      block attention mass and within-block logit variation, approximated
+ *      from compact block statistics; review "Summary", paper Section 3,
+ *      Eqs. 4-7.
+ *   3. ckv_compensated_decode_attention: exact attention over the selected
+ *      blocks' tokens; every omitted block enters the softmax once, with its
+ *      block-mean logit, weighted by its token count, carrying its mean
+ *      value ("Mean compensation", review "Summary").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller.  The
+ *   library allocates no memory and keeps no state between calls, except a
+ *   thread-local text describing the last argument error (ckv_last_error).
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Work is enqueued asynchronously on it; nothing synchronizes the host.
+ * - Arguments are validated on the host before anything is enqueued.  An
+ *   invalid or unsupported argument returns an error status and enqueues
+ *   nothing.  A failed kernel launch returns CKV_ERR_HIP.  Faults inside a
+ *   kernel surface at the caller's next synchronization.
+ * - Device-side contents (seq_lens, block_table, selected) cannot be checked
+ *   on the host.  Kernels clamp seq_lens[b] to [0, max_blocks_per_seq *
+ *   block_size] and skip page ids outside [0, num_pages) and block ids
+ *   outside [0, num_blocks), so invalid contents give unspecified results
+ *   but never an out-of-bounds access.
+ * - Inputs must be finite; non-finite inputs give unspecified results.
+ * - The library is reentrant; calls on different streams with disjoint
+ *   outputs and workspaces may overlap.
+ *
+ * Layouts (row-major, innermost last)
+ * -----------------------------------
+ *   q           [B][Hq][d]                 kv_dtype
+ *   k_cache     [P][Hkv][block_size][d]    kv_dtype  (one page = one block)
+ *   v_cache     [P][Hkv][block_size][d]    kv_dtype
+ *   block_table [B][max_blocks_per_seq]    int32     logical block -> page
+ *   seq_lens    [B]                        int32     tokens per sequence
+ *   mean_k      [P][Hkv][d]                kv_dtype  (summaries are indexed by page)
+ *   mean_v      [P][Hkv][d]                kv_dtype
+ *   gvar        [P][Hkv][r]                float32
+ *   count       [P]                        int32
+ *   selected    [B][Hkv][k_max]            int32, k_max = min(max_blocks_per_seq, budget/block_size)
+ *   out         [B][Hq][d]                 float32
+ *   lse         [B][Hq]                    float32 (natural log)
+ * Query head h reads KV head h / (Hq / Hkv).  Block i of a sequence holds
+ * tokens [i*block_size, min((i+1)*block_size, L)).
+ */
+#ifndef COMPKV_H
+#define COMPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CKV_OK = 0,
+  CKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent dims */
+  CKV_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+  CKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  CKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} ckv_status;
+
+typedef enum { CKV_BF16 = 0, CKV_F32 = 1 } ckv_dtype;
+
+/* Which score ranks the blocks.
+ *   CKV_SCORE_COMPKV: practical residual score, S = A * var_hat / 2 with the
+ *     second-order mass estimate A = n exp(s_bar) (1 + var_hat / 2)
+ *     (review "Summary"; abstract).
+ *   CKV_SCORE_MASS: estimated attention mass A alone - the score that
+ *     remains when compensation is removed from the objective (review "Key
+ *     claims", App. A.5).
+ * For GQA the ranked score of a block is the sum over the KV head's query
+ * heads of score / Z_hat, Z_hat = sum over the sequence's blocks of A. */
+typedef enum { CKV_SCORE_COMPKV = 0, CKV_SCORE_MASS = 1 } ckv_score_mode;
+
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv in {1, 2, 4, 8} */
+  int32_t head_dim;           /* d in {64, 128} */
+  int32_t block_size;         /* tokens per block and per page; 16 */
+  int32_t r_groups;           /* r >= 1, d % r == 0: channel groups of the key variance */
+  int32_t num_pages;          /* P >= 1: pages of the cache and of the summary store */
+  int32_t max_blocks_per_seq; /* columns of block_table, 1 .. 15872 */
+  int32_t kv_dtype;           /* ckv_dtype of q, k_cache, v_cache, mean_k, mean_v */
+} ckv_dims;
+
+typedef struct {
+  void* mean_k;   /* [P][Hkv][d] kv_dtype: mean key of the page's tokens */
+  void* mean_v;   /* [P][Hkv][d] kv_dtype: mean value */
+  float* gvar;    /* [P][Hkv][r]: per channel group, the mean of the channels'
+                     population variances of the keys */
+  int32_t* count; /* [P]: tokens in the page */
+} ckv_summaries;
+
+/* Build block summaries from the paged cache (review "Summary", FAQ).
+ *
+ * append_only == 0 (prefill, bulk): every block of every sequence.
+ * append_only != 0 (decode): only the block holding each sequence's last
+ *   token, i.e. the block a newly appended token entered.  It is recomputed
+ *   from its raw tokens, so bulk and append give identical bits.
+ * Means are accumulated in float32 and rounded to kv_dtype (nearest, ties to
+ * even); variances are two-pass (population, divide by n) in float32.
+ * Summaries of pages not touched are left unchanged.
+ * Errors: CKV_ERR_INVALID_ARG / CKV_ERR_UNSUPPORTED for bad dims or null
+ * pointers (nothing enqueued); CKV_ERR_HIP if the launch fails. */
+ckv_status ckv_build_summaries(const ckv_dims* dims, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t append_only, const ckv_summaries* summaries,
+                               void* stream);
+
+/* Bytes of device workspace that ckv_score_select and
+ * ckv_compensated_decode_attention need for these dims and this budget
+ * (0 when dims are invalid).  The same workspace must be passed to both
+ * calls of one decode step. */
+size_t ckv_workspace_bytes(const ckv_dims* dims, int32_t budget_tokens);
+
+/* Score every block and select the top-k per (sequence, KV head) under a
+ * token budget (abstract; review "Summary", Section 3 Eqs. 4-7).
+ *
+ * k = min(num_blocks, budget_tokens / block_size), num_blocks =
+ * ceil(seq_lens[b] / block_size); a partial tail block counts as one block.
+ * Ties go to the lower block index.  selected[b][g][0..k) receives the
+ * chosen logical block ids in ascending order; entries k..k_max-1 are set to
+ * -1.  num_selected[b][g] = k.
+ * group_scores: optional (may be NULL); if given, [B][Hkv][max_blocks_per_seq]
+ * float32 receives the ranked score of each block (entries past num_blocks
+ * are not written).  The workspace keeps, for the attention call that
+ * follows, the per-block log-scores and the compensation partials of all
+ * blocks.
+ * Errors: as ckv_build_summaries, plus CKV_ERR_WORKSPACE. */
+ckv_status ckv_score_select(const ckv_dims* dims, const void* q, const ckv_summaries* summaries,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t budget_tokens, int32_t score_mode, int32_t* selected,
+                            int32_t* num_selected, float* group_scores, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Exact attention over the selected blocks plus Mean compensation of the
+ * omitted ones (abstract; review "Summary").
+ *
+ * For query head h: every token j of a selected block contributes weight
+ * exp(tau q.k_j) and value v_j (tau = 1/sqrt(d)); if `compensate` != 0 every
+ * omitted block i contributes weight n_i exp(tau q.mean_k_i) and value
+ * mean_v_i.  out = weighted mean of the values, lse = log of the total
+ * weight.  When every block is selected the result is dense attention; with
+ * nothing to attend to, out = 0 and lse = -inf.
+ * `selected`/`num_selected` are as written by ckv_score_select (any set of
+ * distinct ascending block ids is accepted).  The workspace must hold what
+ * ckv_score_select wrote in this step for the same q and summaries.
+ * lse may be NULL.  Errors: as ckv_score_select. */
+ckv_status ckv_compensated_decode_attention(const ckv_dims* dims, const void* q,
+                                            const void* k_cache, const void* v_cache,
+                                            const ckv_summaries* summaries,
+                                            const int32_t* block_table, const int32_t* seq_lens,
+                                            int32_t budget_tokens, const int32_t* selected,
+                                            const int32_t* num_selected, int32_t compensate,
+                                            float* out, float* lse, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/* One whole decode step: ckv_score_select followed by
+ * ckv_compensated_decode_attention with compensation on, same arguments and
+ * results (group scores are not written). */
+ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_cache,
+                           const void* v_cache, const ckv_summaries* summaries,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t budget_tokens, int32_t score_mode, int32_t* selected,
+                           int32_t* num_selected, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Dense decode attention over every token (the baseline the method is
+ * measured against: review "Summary", speed-up over full attention).
+ * Workspace from ckv_dense_workspace_bytes.  lse may be NULL. */
+size_t ckv_dense_workspace_bytes(const ckv_dims* dims);
+ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_table,
+                                      const int32_t* seq_lens, float* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* ckv_status_string(ckv_status status);
+
+/* Text describing the last argument error returned on this thread ("" if none). */
+const char* ckv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMPKV_H */

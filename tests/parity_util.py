@@ -1,0 +1,201 @@
+"""Run one decode step on the GPU (through the C ABI) and in the CPU oracle on
+the same generated inputs, and compare them.
+
+Tolerances:
+  summaries  mean key / mean value: within 1 unit in the last place of the
+             KV dtype (bf16: the GPU accumulates in fp32, then rounds; the
+             oracle rounds the exact mean once); f32 storage: 2e-6 relative.
+             grouped variance: 1e-5 relative (fp32 two-pass sums of <= 16
+             terms, then a mean over <= 128 channels).
+  selection  block ids bit-exact.  (a) against a CPU top-k of the GPU's own
+             fp32 scores (the decision in the kernel's precision); (b)
+             against the oracle's fp64 selection wherever the oracle's k-th
+             and (k+1)-th scores differ by more than NEAR_TIE relative;
+             closer boundaries are reported and the GPU set is checked to be
+             a valid top-k within NEAR_TIE.
+  output     2e-3 max-abs (bf16 inputs, fp32 accumulation); lse 1e-4 abs.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from compensated_kv_selection_amd import compkv as C
+from compensated_kv_selection_amd.tensors import to_device, torch_to_storage
+from compensated_kv_selection_amd.workloads import DecodeInputs
+from oracle import compkv_oracle as O
+
+NEAR_TIE = 1e-5
+OUT_ATOL = 2e-3
+LSE_ATOL = 1e-4
+
+
+@dataclasses.dataclass
+class GpuResult:
+    mean_k: np.ndarray   # storage dtype, [P, Hkv, d]
+    mean_v: np.ndarray
+    gvar: np.ndarray
+    count: np.ndarray
+    selected: np.ndarray     # [B, Hkv, kmax]
+    num_selected: np.ndarray  # [B, Hkv]
+    group_scores: Optional[np.ndarray]  # [B, Hkv, max_blocks] float32
+    out: np.ndarray          # [B, Hq, d]
+    lse: np.ndarray          # [B, Hq]
+
+
+def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.SCORE_COMPKV,
+            compensate: bool = True, fused: bool = False, device="cuda:0", dev=None,
+            summaries=None) -> GpuResult:
+    budget = w.budget_tokens if budget is None else budget
+    dev = dev or to_device(w, device)
+    dims = dev.dims
+    if summaries is None:
+        summaries = C.allocate_summaries(dims, device)
+        C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summaries)
+    ws = C.allocate_workspace(C.workspace_bytes(dims, budget), device)
+    gs = None
+    if fused:
+        sel, nsel, out, lse = C.decode_step(dims, dev.q, dev.k_cache, dev.v_cache, summaries,
+                                            dev.block_table, dev.seq_lens, budget, ws, score_mode)
+    else:
+        gs = torch.full((dims.batch, dims.num_kv_heads, dims.max_blocks_per_seq), float("nan"),
+                        dtype=torch.float32, device=device)
+        sel, nsel = C.score_select(dims, dev.q, summaries, dev.block_table, dev.seq_lens, budget, ws,
+                                   score_mode, group_scores=gs)
+        out, lse = C.compensated_decode_attention(dims, dev.q, dev.k_cache, dev.v_cache, summaries,
+                                                  dev.block_table, dev.seq_lens, budget, sel, nsel, ws,
+                                                  compensate=compensate)
+    torch.cuda.synchronize()
+    return GpuResult(torch_to_storage(summaries.mean_k), torch_to_storage(summaries.mean_v),
+                     summaries.gvar.cpu().numpy(), summaries.count.cpu().numpy(),
+                     sel.cpu().numpy(), nsel.cpu().numpy(),
+                     None if gs is None else gs.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy())
+
+
+@dataclasses.dataclass
+class OracleSeq:
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    summ: O.Summaries
+    step: O.StepResult
+
+
+ORACLE_MODES = {C.SCORE_COMPKV: "compkv", C.SCORE_MASS: "mass_hat"}
+
+
+def run_oracle(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.SCORE_COMPKV,
+               compensate: bool = True, seqs=None) -> List[Optional[OracleSeq]]:
+    budget = w.budget_tokens if budget is None else budget
+    res = []
+    for b in range(w.batch):
+        if seqs is not None and b not in seqs:
+            res.append(None)
+            continue
+        q, k, v = O.sequence_arrays(w.q[b], w.k_tokens[b], w.v_tokens[b], w.dtype)
+        summ = O.build_summaries(k, v, w.block_size, w.r_groups, w.dtype)
+        step = O.decode_step(q, k, v, summ, budget_tokens=budget, block_size=w.block_size,
+                             r=w.r_groups, score_mode=ORACLE_MODES[score_mode], compensate=compensate)
+        res.append(OracleSeq(q, k, v, summ, step))
+    return res
+
+
+def _ordered_bf16(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def _oracle_bf16_bits(x: np.ndarray) -> np.ndarray:
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def check_summaries(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]]) -> None:
+    for b, o in enumerate(ora):
+        if o is None:
+            continue
+        M = w.num_blocks(b)
+        pages = w.block_table[b, :M]
+        gk, gv_, gg, gc = g.mean_k[pages], g.mean_v[pages], g.gvar[pages], g.count[pages]
+        np.testing.assert_array_equal(gc, o.summ.count, err_msg=f"count seq {b}")
+        if w.dtype == "bf16":
+            for name, gpu, ref in (("mean_k", gk, o.summ.mean_k), ("mean_v", gv_, o.summ.mean_v)):
+                d = np.abs(_ordered_bf16(gpu) - _ordered_bf16(_oracle_bf16_bits(ref)))
+                assert d.max() <= 1, f"{name} seq {b}: {d.max()} bf16 ulps apart"
+        else:
+            np.testing.assert_allclose(gk, o.summ.mean_k, rtol=2e-6, atol=2e-6, err_msg=f"mean_k seq {b}")
+            np.testing.assert_allclose(gv_, o.summ.mean_v, rtol=2e-6, atol=2e-6, err_msg=f"mean_v seq {b}")
+        np.testing.assert_allclose(gg, o.summ.gvar, rtol=1e-5, atol=1e-7, err_msg=f"gvar seq {b}")
+
+
+def cpu_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    order = np.lexsort((np.arange(scores.size), -scores))
+    return np.sort(order[:k])
+
+
+def check_selection_isolated(w: DecodeInputs, g: GpuResult, budget: int) -> None:
+    """GPU selection == CPU top-k over the GPU's own fp32 scores, bit-exact."""
+    kmax = min(w.max_blocks, budget // w.block_size)
+    for b in range(w.batch):
+        M = w.num_blocks(b)
+        kk = min(M, kmax)
+        for h in range(w.num_kv_heads):
+            assert g.num_selected[b, h] == kk
+            s = g.group_scores[b, h, :M]
+            assert np.all(np.isfinite(s)) and np.all(s >= 0)
+            np.testing.assert_array_equal(g.selected[b, h, :kk], cpu_topk(s, kk), err_msg=f"seq {b} head {h}")
+            if kmax > kk:
+                assert np.all(g.selected[b, h, kk:kmax] == -1)
+
+
+def check_selection_vs_oracle(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]],
+                              report: Optional[list] = None) -> int:
+    """Returns the number of (seq, KV head) boundaries that were near-ties."""
+    near = 0
+    for b, o in enumerate(ora):
+        if o is None:
+            continue
+        kk = o.step.selected.shape[1]
+        for h in range(w.num_kv_heads):
+            gsel = g.selected[b, h, :kk]
+            osel = o.step.selected[h]
+            if o.step.gaps[h] >= NEAR_TIE:
+                np.testing.assert_array_equal(gsel, osel, err_msg=f"seq {b} KV head {h}")
+            else:
+                near += 1
+                rank = o.step.rank_score[h]
+                kth = np.sort(rank)[::-1][kk - 1]
+                must = np.nonzero(rank > kth * (1 + NEAR_TIE))[0]
+                assert set(must.tolist()) <= set(gsel.tolist()), f"seq {b} head {h}: missed a clear winner"
+                assert np.all(rank[gsel] >= kth * (1 - NEAR_TIE)), f"seq {b} head {h}: took a clear loser"
+                if report is not None:
+                    report.append((b, h, float(o.step.gaps[h]), bool(np.array_equal(gsel, osel))))
+    return near
+
+
+def oracle_output_for(o: OracleSeq, selected: np.ndarray, w: DecodeInputs, compensate: bool = True):
+    return O.compensated_attention(o.q, o.k, o.v, o.summ, selected, w.block_size, compensate)
+
+
+def check_outputs(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]],
+                  compensate: bool = True) -> float:
+    """Compare with the oracle's attention on the GPU's own selection; return max abs error."""
+    worst = 0.0
+    for b, o in enumerate(ora):
+        if o is None:
+            continue
+        kk = o.step.selected.shape[1]
+        sel = g.selected[b, :, :kk].astype(np.int64)
+        out, lse = oracle_output_for(o, sel, w, compensate)
+        err = np.abs(g.out[b] - out).max()
+        worst = max(worst, float(err))
+        assert err <= OUT_ATOL, f"seq {b}: out max abs error {err}"
+        fin = np.isfinite(lse)
+        np.testing.assert_array_equal(np.isfinite(g.lse[b]), fin)
+        if fin.any():
+            lerr = np.abs(g.lse[b][fin] - lse[fin]).max()
+            assert lerr <= LSE_ATOL, f"seq {b}: lse error {lerr}"
+    return worst

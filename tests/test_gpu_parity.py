@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Needs an MI355X and the built library."""
+import numpy as np
+import pytest
+import torch
+
+from compensated_kv_selection_amd import compkv as C
+from compensated_kv_selection_amd import workloads as W
+from compensated_kv_selection_amd.tensors import to_device
+from oracle import compkv_oracle as O
+
+from parity_util import (check_outputs, check_selection_isolated, check_selection_vs_oracle,
+                         check_summaries, run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    C.load_library()  # raises if libcompkv.so is not built
+    yield
+
+
+def full_check(w, budget=None, score_mode=C.SCORE_COMPKV, compensate=True, fused=False, report=None):
+    budget = w.budget_tokens if budget is None else budget
+    print(f"[case] {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+          f"d={w.head_dim} r={w.r_groups} {w.dtype} lens={list(w.seq_lens)[:6]} budget={budget} "
+          f"mode={score_mode} comp={compensate} fused={fused}", flush=True)
+    g = run_gpu(w, budget, score_mode, compensate, fused=fused)
+    ora = run_oracle(w, budget, score_mode, compensate)
+    check_summaries(w, g, ora)
+    if not fused:
+        check_selection_isolated(w, g, budget)
+    near = check_selection_vs_oracle(w, g, ora, report)
+    err = check_outputs(w, g, ora, compensate)
+    print(f"[case] ok: max |out - oracle| = {err:.2e}, near-ties {near}", flush=True)
+    return g, ora
+
+
+def small_gqa(seed=0, **kw):
+    cfg = dict(seq_lens=[1000, 777, 16, 1, 4097], num_q_heads=8, num_kv_heads=2, head_dim=128,
+               r_groups=4, budget_tokens=128, dtype="bf16", n_needles=0, n_outliers=2, seed=seed)
+    cfg.update(kw)
+    return W.make_decode_inputs(name="small_gqa", **cfg)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_tiny_single_head_f32(seed):
+    full_check(W.make_preset("tiny", seed=seed))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_small_gqa_ragged_bf16(seed):
+    full_check(small_gqa(seed))
+
+
+@pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (2, 64, "f32"), (4, 64, "bf16"),
+                                       (8, 128, "bf16"), (8, 64, "f32"), (2, 128, "f32")])
+def test_head_layouts(G, d, dtype):
+    w = W.make_decode_inputs(name=f"G{G}", seq_lens=[2500, 333], num_q_heads=2 * G, num_kv_heads=2,
+                             head_dim=d, r_groups=4, budget_tokens=160, dtype=dtype, n_needles=3,
+                             n_outliers=1, seed=G * 10 + d)
+    full_check(w)
+
+
+@pytest.mark.parametrize("r", [1, 2, 8, 16, 64, 128])
+def test_r_groups(r):
+    full_check(small_gqa(seed=7, r_groups=r))
+
+
+@pytest.mark.parametrize("budget", [0, 15, 16, 48, 4096, 100_000])
+def test_budget_edges(budget):
+    # 0 and 15: nothing selected, every block compensated; 4096+: every block
+    # of the shorter sequences selected (dense); 100000: all blocks, all sequences.
+    full_check(small_gqa(seed=3), budget=budget)
+
+
+@pytest.mark.parametrize("budget", [0, 64, 100_000])
+def test_without_compensation(budget):
+    full_check(small_gqa(seed=4), budget=budget, compensate=False)
+
+
+@pytest.mark.parametrize("budget", [64, 256])
+def test_mass_score_mode(budget):
+    full_check(small_gqa(seed=5), budget=budget, score_mode=C.SCORE_MASS)
+
+
+def test_fused_step_matches():
+    w = small_gqa(seed=6)
+    g1, _ = full_check(w)
+    g2 = run_gpu(w, fused=True)
+    np.testing.assert_array_equal(g1.selected, g2.selected)
+    np.testing.assert_array_equal(g1.out, g2.out)
+    np.testing.assert_array_equal(g1.lse, g2.lse)
+
+
+def test_constant_key_blocks_give_dense_output():
+    # Zero within-block variance: every score is 0, ties go to the lowest ids,
+    # and compensation is exact, so the output equals dense attention.
+    w = small_gqa(seed=8, seq_lens=[640, 100])
+    for b in range(w.batch):
+        k = w.k_tokens[b]
+        L = k.shape[0]
+        for i in range(0, L, 16):
+            k[i:i + 16] = k[i]
+    g = run_gpu(w, budget=64)
+    for b in range(w.batch):
+        M = w.num_blocks(b)
+        assert np.all(g.group_scores[b, :, :M] == 0)
+        np.testing.assert_array_equal(g.selected[b, :, :4], np.tile(np.arange(4), (2, 1)))
+        q, k, v = O.sequence_arrays(w.q[b], w.k_tokens[b], w.v_tokens[b], w.dtype)
+        out, lse = O.dense_attention(q, k, v)
+        assert np.abs(g.out[b] - out).max() <= 2e-3
+        assert np.abs(g.lse[b] - lse).max() <= 1e-4
+
+
+def test_dense_kernel_matches_oracle():
+    w = small_gqa(seed=9)
+    dev = to_device(w)
+    ws = C.allocate_workspace(C.dense_workspace_bytes(dev.dims), "cuda:0")
+    out, lse = C.dense_decode_attention(dev.dims, dev.q, dev.k_cache, dev.v_cache, dev.block_table,
+                                        dev.seq_lens, ws)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.batch):
+        q, k, v = O.sequence_arrays(w.q[b], w.k_tokens[b], w.v_tokens[b], w.dtype)
+        ro, rl = O.dense_attention(q, k, v)
+        assert np.abs(out[b] - ro).max() <= 2e-3
+        assert np.abs(lse[b] - rl).max() <= 1e-4
+
+
+def test_append_matches_bulk_bit_exact():
+    # Decode-time append recomputes the tail block from raw tokens: after a
+    # chain of appends the store equals a bulk build of the final cache.
+    w = W.make_decode_inputs(name="append", seq_lens=[40, 16, 1], num_q_heads=4, num_kv_heads=2,
+                             head_dim=128, r_groups=4, budget_tokens=32, dtype="bf16", n_needles=0,
+                             n_outliers=1, seed=11, extra_capacity_tokens=40)
+    steps = W.make_append_steps(w, 35, seed=12)
+    full = W.make_decode_inputs(name="append", seq_lens=[40, 16, 1], num_q_heads=4, num_kv_heads=2,
+                                head_dim=128, r_groups=4, budget_tokens=32, dtype="bf16", n_needles=0,
+                                n_outliers=1, seed=11, extra_capacity_tokens=40)
+    for s in steps:
+        W.append_tokens(full, s)
+    kc, vc = full.paged_cache()
+    dev = to_device(full, k_cache=kc, v_cache=vc)
+    dims = dev.dims
+    bulk = C.allocate_summaries(dims, "cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, bulk)
+    inc = C.allocate_summaries(dims, "cuda:0")
+    lens = torch.tensor([40, 16, 1], dtype=torch.int32, device="cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, lens, inc)
+    for _ in steps:
+        lens += 1
+        C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, lens, inc, append_only=True)
+    torch.cuda.synchronize()
+    for b in range(3):
+        pages = torch.from_numpy(full.block_table[b, :full.num_blocks(b)]).long().cuda()
+        for name in ("mean_k", "mean_v", "gvar"):
+            assert torch.equal(getattr(bulk, name)[pages], getattr(inc, name)[pages]), name
+        assert torch.equal(bulk.count[pages], inc.count[pages])
+    g = run_gpu(full, dev=dev, summaries=inc)
+    ora = run_oracle(full)
+    check_summaries(full, g, ora)
+    check_selection_vs_oracle(full, g, ora)
+    check_outputs(full, g, ora)
+
+
+def test_repeat_runs_are_bit_identical():
+    w = small_gqa(seed=13)
+    a = run_gpu(w)
+    b = run_gpu(w)
+    for name in ("mean_k", "mean_v", "gvar", "selected", "group_scores", "out", "lse"):
+        np.testing.assert_array_equal(getattr(a, name), getattr(b, name), err_msg=name)
+
+
+# ---- full-size workloads -------------------------------------------------------
+
+
+def test_llama_32k():
+    full_check(W.make_preset("llama_32k", seed=0), fused=True)
+
+
+def test_llama_128k_headline():
+    report = []
+    full_check(W.make_preset("llama_128k", seed=0), fused=True, report=report)
+    print("near-ties:", report, flush=True)
+
+
+def test_llama_128k_headline_unfused_scores():
+    full_check(W.make_preset("llama_128k", seed=1))
+
+
+def test_batched_ragged():
+    full_check(W.make_preset("batched_ragged", seed=0), fused=True)
+
+
+def test_prefill_then_decode_loop():
+    # Bulk summaries over 128K tokens, then 64 decode steps that each append one
+    # token (tail-block summary update) and run the compensated step with a
+    # 2048-token budget; checked against the oracle at several steps.
+    w = W.make_preset("prefill_128k_loop", seed=0)
+    steps = W.make_append_steps(w, 64, seed=21)
+    kc, vc = w.paged_cache()
+    dev = to_device(w, k_cache=kc, v_cache=vc)
+    del kc, vc
+    dims = dev.dims
+    summ = C.allocate_summaries(dims, "cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
+    L0 = int(w.seq_lens[0])
+    _, k0, v0 = O.sequence_arrays(w.q[0], w.k_tokens[0], w.v_tokens[0], w.dtype)
+    k64 = np.zeros((L0 + len(steps), 8, 128))
+    v64 = np.zeros_like(k64)
+    k64[:L0], v64[:L0] = k0, v0
+    del k0, v0
+    osumm = O.build_summaries(k64[:L0], v64[:L0], 16, 4, "bf16")
+    ws = C.allocate_workspace(C.workspace_bytes(dims, w.budget_tokens), "cuda:0")
+    checkpoints = {0, 1, 15, 16, 63}
+    for t, st in enumerate(steps):
+        L = L0 + t
+        p, slot = int(w.block_table[0, L // 16]), L % 16
+        dev.k_cache[p, :, slot, :] = torch.from_numpy(st.k_new[0].view(np.int16)).view(torch.bfloat16).cuda()
+        dev.v_cache[p, :, slot, :] = torch.from_numpy(st.v_new[0].view(np.int16)).view(torch.bfloat16).cuda()
+        dev.seq_lens.fill_(L + 1)
+        dev.q.copy_(torch.from_numpy(st.q.view(np.int16)).view(torch.bfloat16))
+        C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ,
+                          append_only=True)
+        sel, nsel, out, lse = C.decode_step(dims, dev.q, dev.k_cache, dev.v_cache, summ, dev.block_table,
+                                            dev.seq_lens, w.budget_tokens, ws)
+        k64[L] = O.widen(st.k_new[0], "bf16")
+        v64[L] = O.widen(st.v_new[0], "bf16")
+        osumm = O.append_summaries(osumm, k64[:L + 1], v64[:L + 1], 16, 4, "bf16")
+        if t in checkpoints:
+            torch.cuda.synchronize()
+            print(f"[case] decode step {t}: L={L + 1}", flush=True)
+            q = O.widen(st.q[0], "bf16")
+            res = O.decode_step(q, k64[:L + 1], v64[:L + 1], osumm, budget_tokens=w.budget_tokens,
+                                block_size=16, r=4)
+            g_sel = sel.cpu().numpy()[0]
+            kk = res.selected.shape[1]
+            assert np.all(nsel.cpu().numpy()[0] == kk)
+            for h in range(8):
+                if res.gaps[h] >= 1e-5:
+                    np.testing.assert_array_equal(g_sel[h, :kk], res.selected[h])
+            o2, l2 = O.compensated_attention(q, k64[:L + 1], v64[:L + 1], osumm,
+                                             g_sel[:, :kk].astype(np.int64), 16)
+            assert np.abs(out.cpu().numpy()[0] - o2).max() <= 2e-3
+            assert np.abs(lse.cpu().numpy()[0] - l2).max() <= 1e-4
+            M = -(-(L + 1) // 16)
+            page = int(w.block_table[0, M - 1])
+            assert summ.count[page].item() == osumm.count[M - 1]
