@@ -169,8 +169,21 @@ def dense_workspace_bytes(dims: Dims) -> int:
 
 
 def allocate_workspace(nbytes: int, device) -> torch.Tensor:
-    # torch's caching allocator returns blocks aligned to at least 512 bytes
-    return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+    """Zero-filled workspace (the step kernel's control words must start at
+    zero; every call leaves them zero).  torch's caching allocator returns
+    blocks aligned to at least 512 bytes."""
+    return torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+
+CTRL_WORDS_HEADER = 64
+
+
+def workspace_control(ws: torch.Tensor, batch: int, num_kv_heads: int) -> torch.Tensor:
+    """The workspace's control words as int32 (host copy): [ticket, done,
+    error flag, ...] then four counters per (sequence, KV head).  All are zero
+    between calls; the error flag is set if a bounded wait ever ran out."""
+    n = CTRL_WORDS_HEADER + 4 * batch * num_kv_heads
+    return ws[: 4 * n].view(torch.int32).cpu()
 
 
 def score_select(dims: Dims, q, summaries: Summaries, block_table, seq_lens, budget_tokens: int,

@@ -70,27 +70,45 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.max_blocks = d->max_blocks_per_seq;
   const int kb = budget_tokens < 0 ? 0 : budget_tokens / d->block_size;
   x.kmax = kb < x.max_blocks ? kb : x.max_blocks;
-  x.n_chunks = (x.max_blocks + ckv::kScanChunk - 1) / ckv::kScanChunk;
-  x.n_splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
+  x.n_chunks = (x.max_blocks + ckv::kChunk - 1) / ckv::kChunk;
+  x.n_slices = (x.max_blocks + ckv::kSlice - 1) / ckv::kSlice;
+  int splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
+  splits = splits < 1 ? 1 : (splits > ckv::kMaxSplits ? ckv::kMaxSplits : splits);
+  x.n_splits = splits;
+  x.pages_per_split = x.kmax > 0 ? (x.kmax + splits - 1) / splits : 1;
   x.dtype = d->kv_dtype;
   x.tau = (float)(1.0 / sqrt((double)d->head_dim));
   x.tau2 = (float)(1.0 / (double)d->head_dim);
+  if (G * (x.n_chunks + 2 * x.n_splits) > ckv::kMergeFactors)
+    return fail(CKV_ERR_UNSUPPORTED, "too many partials for the merge");
   return CKV_OK;
 }
 
 struct Layout {
-  size_t comp, lam, gath, total;
+  size_t ctrl, xs, cpart, cand, gpart, total;
 };
 
+size_t ctrl_bytes(const ckv::Shape& s) {
+  return align_up((size_t)(ckv::kCtrlHeader + 4 * s.B * s.Hkv) * sizeof(uint32_t));
+}
+
+// Sparse-step workspace: control words, per-block scores, scan partials,
+// first-level select candidates, gather partials.
 Layout layout(const ckv::Shape& s) {
   Layout L;
   const size_t pst = ckv::kPartStride(s.D);
-  L.comp = 0;
-  size_t off = align_up((size_t)s.B * s.Hkv * s.n_chunks * s.G * pst * sizeof(float));
-  L.lam = off;
+  const size_t bg = (size_t)s.B * s.Hkv;
+  size_t off = 0;
+  L.ctrl = off;
+  off += ctrl_bytes(s);
+  L.xs = off;
   off += align_up((size_t)s.B * s.Hq * s.max_blocks * sizeof(float));
-  L.gath = off;
-  off += align_up((size_t)s.B * s.Hkv * s.n_splits * s.G * 2 * pst * sizeof(float));
+  L.cpart = off;
+  off += align_up(bg * s.n_chunks * s.G * pst * sizeof(float));
+  L.cand = off;
+  off += align_up(bg * s.n_slices * (size_t)(s.kmax > 0 ? s.kmax : 1) * sizeof(uint64_t));
+  L.gpart = off;
+  off += align_up(bg * s.n_splits * s.G * 2 * pst * sizeof(float));
   L.total = off;
   return L;
 }
@@ -98,8 +116,19 @@ Layout layout(const ckv::Shape& s) {
 ckv::Work carve(const ckv::Shape& s, void* ws) {
   const Layout L = layout(s);
   char* base = static_cast<char*>(ws);
-  return ckv::Work{reinterpret_cast<float*>(base + L.comp), reinterpret_cast<float*>(base + L.lam),
-                   reinterpret_cast<float*>(base + L.gath)};
+  return ckv::Work{reinterpret_cast<uint32_t*>(base + L.ctrl), reinterpret_cast<float*>(base + L.xs),
+                   reinterpret_cast<float*>(base + L.cpart), reinterpret_cast<uint64_t*>(base + L.cand),
+                   reinterpret_cast<float*>(base + L.gpart)};
+}
+
+void set_dense(ckv::Shape& s) {
+  s.pages_per_split = ckv::kDensePages;
+  s.n_splits = (s.max_blocks + ckv::kDensePages - 1) / ckv::kDensePages;
+}
+
+size_t dense_bytes(const ckv::Shape& s) {
+  return ctrl_bytes(s) + align_up((size_t)s.B * s.Hkv * s.n_splits * s.G * ckv::kPartStride(s.D) *
+                                  sizeof(float));
 }
 
 ckv_status check_summaries(const ckv_summaries* sm) {
@@ -187,12 +216,11 @@ ckv_status ckv_score_select(const ckv_dims* dims, const void* q, const ckv_summa
     return fail(CKV_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
   CKV_TRY(check_summaries(summaries));
   CKV_TRY(check_workspace(s, workspace, workspace_bytes));
-  const ckv::Work w = carve(s, workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = ckv::launch_scan(s, q, to_summ(summaries), block_table, seq_lens, score_mode, w, st);
-  if (e != hipSuccess) return hip_status(e, "scan launch");
-  return hip_status(ckv::launch_select(s, seq_lens, w, selected, num_selected, group_scores, st),
-                    "select launch");
+  ckv::StepIO io{q, nullptr, nullptr, to_summ(summaries), block_table, seq_lens, selected,
+                 num_selected, group_scores, nullptr, nullptr, score_mode, 1};
+  return hip_status(ckv::launch_step(s, ckv::kModeSelectOnly, io, carve(s, workspace),
+                                     static_cast<hipStream_t>(stream)),
+                    "score/select launch");
 }
 
 ckv_status ckv_compensated_decode_attention(const ckv_dims* dims, const void* q,
@@ -213,14 +241,12 @@ ckv_status ckv_compensated_decode_attention(const ckv_dims* dims, const void* q,
   if (!out) return fail(CKV_ERR_INVALID_ARG, "out is NULL");
   CKV_TRY(check_summaries(summaries));
   CKV_TRY(check_workspace(s, workspace, workspace_bytes));
-  const ckv::Work w = carve(s, workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = ckv::launch_gather(s, q, k_cache, v_cache, to_summ(summaries), block_table,
-                                    seq_lens, selected, num_selected, compensate ? 1 : 0, w, st);
-  if (e != hipSuccess) return hip_status(e, "gather launch");
-  return hip_status(
-      ckv::launch_merge(s, seq_lens, num_selected, compensate ? 1 : 0, w, out, lse, st),
-      "merge launch");
+  ckv::StepIO io{q, k_cache, v_cache, to_summ(summaries), block_table, seq_lens,
+                 const_cast<int32_t*>(selected), const_cast<int32_t*>(num_selected), nullptr, out,
+                 lse, 0, compensate ? 1 : 0};
+  return hip_status(ckv::launch_step(s, ckv::kModeAttendOnly, io, carve(s, workspace),
+                                     static_cast<hipStream_t>(stream)),
+                    "attention launch");
 }
 
 ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_cache,
@@ -229,20 +255,30 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                            int32_t budget_tokens, int32_t score_mode, int32_t* selected,
                            int32_t* num_selected, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  if (!k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "k_cache or v_cache is NULL");
+  if (budget_tokens < 0) return fail(CKV_ERR_INVALID_ARG, "budget_tokens must be >= 0");
+  ckv::Shape s;
+  CKV_TRY(make_shape(dims, budget_tokens, &s));
+  if (!q || !k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "q, k_cache or v_cache is NULL");
+  if (!block_table || !seq_lens) return fail(CKV_ERR_INVALID_ARG, "block_table or seq_lens is NULL");
+  if (!num_selected || (!selected && s.kmax > 0))
+    return fail(CKV_ERR_INVALID_ARG, "selected or num_selected is NULL");
   if (!out) return fail(CKV_ERR_INVALID_ARG, "out is NULL");
-  CKV_TRY(ckv_score_select(dims, q, summaries, block_table, seq_lens, budget_tokens, score_mode,
-                           selected, num_selected, nullptr, workspace, workspace_bytes, stream));
-  return ckv_compensated_decode_attention(dims, q, k_cache, v_cache, summaries, block_table,
-                                          seq_lens, budget_tokens, selected, num_selected, 1, out,
-                                          lse, workspace, workspace_bytes, stream);
+  if (score_mode != CKV_SCORE_COMPKV && score_mode != CKV_SCORE_MASS)
+    return fail(CKV_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+  CKV_TRY(check_summaries(summaries));
+  CKV_TRY(check_workspace(s, workspace, workspace_bytes));
+  ckv::StepIO io{q, k_cache, v_cache, to_summ(summaries), block_table, seq_lens, selected,
+                 num_selected, nullptr, out, lse, score_mode, 1};
+  return hip_status(ckv::launch_step(s, ckv::kModeFused, io, carve(s, workspace),
+                                     static_cast<hipStream_t>(stream)),
+                    "decode step launch");
 }
 
 size_t ckv_dense_workspace_bytes(const ckv_dims* dims) {
   ckv::Shape s;
   if (make_shape(dims, 0, &s) != CKV_OK) return 0;
-  const int splits = (s.max_blocks + ckv::kDensePages - 1) / ckv::kDensePages;
-  return align_up((size_t)s.B * s.Hkv * splits * s.G * ckv::kPartStride(s.D) * sizeof(float));
+  set_dense(s);
+  return dense_bytes(s);
 }
 
 ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const void* k_cache,
@@ -254,16 +290,19 @@ ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const
   if (!q || !k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "q, k_cache or v_cache is NULL");
   if (!block_table || !seq_lens) return fail(CKV_ERR_INVALID_ARG, "block_table or seq_lens is NULL");
   if (!out) return fail(CKV_ERR_INVALID_ARG, "out is NULL");
-  const size_t need = ckv_dense_workspace_bytes(dims);
+  set_dense(s);
+  const size_t need = dense_bytes(s);
   if (!workspace) return fail(CKV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (workspace_bytes < need)
     return fail(CKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(CKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  s.n_splits = (s.max_blocks + ckv::kDensePages - 1) / ckv::kDensePages;
-  return hip_status(ckv::launch_dense(s, q, k_cache, v_cache, block_table, seq_lens,
-                                      static_cast<float*>(workspace), out, lse,
-                                      static_cast<hipStream_t>(stream)),
+  char* base = static_cast<char*>(workspace);
+  ckv::Work w{reinterpret_cast<uint32_t*>(base), nullptr, nullptr, nullptr,
+              reinterpret_cast<float*>(base + ctrl_bytes(s))};
+  ckv::StepIO io{q, k_cache, v_cache, ckv::Summ{nullptr, nullptr, nullptr, nullptr}, block_table,
+                 seq_lens, nullptr, nullptr, nullptr, out, lse, 0, 0};
+  return hip_status(ckv::launch_step(s, ckv::kModeDense, io, w, static_cast<hipStream_t>(stream)),
                     "dense launch");
 }
 

@@ -9,21 +9,35 @@
 namespace ckv {
 
 constexpr int kBlockSize = 16;      // tokens per block = tokens per page
-constexpr int kScanChunk = 256;     // blocks scored by one scan workgroup
-constexpr int kGatherPages = 4;     // selected blocks attended by one gather workgroup
-constexpr int kDensePages = 32;     // blocks attended by one dense workgroup
-constexpr int kMaxBlocks = 15872;   // select keeps one 32-bit key per block in LDS
+constexpr int kChunk = 256;         // blocks scored by one scan workgroup
+constexpr int kSlice = 1024;        // blocks ranked by one first-level select workgroup
+constexpr int kGatherPages = 4;     // selected blocks per gather workgroup (grows past 64 splits)
+constexpr int kMaxSplits = 64;      // gather workgroups per (sequence, KV head), sparse step
+constexpr int kDensePages = 32;     // blocks per dense workgroup
+constexpr int kMaxBlocks = 15872;   // blocks per sequence (page-table width)
 constexpr int kMaxKvHeads = 64;
-constexpr int kPartStride(int d) { return d + 4; }  // [m, l, z, pad, acc[d]]
+constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks + 2 * splits)
+constexpr int kPartStride(int d) { return d + 4; }  // [m, l, z, c, acc[d]]
+constexpr int kCtrlHeader = 64;     // uint32 words before the per-(sequence, KV head) counters
 
 enum ScoreMode { kScoreCompKV = 0, kScoreMass = 1 };
+
+// What one launch of the step kernel does.
+enum StepMode {
+  kModeFused = 0,       // score, select, gather, merge in one launch
+  kModeSelectOnly = 1,  // score and select; compensation partials stay in the workspace
+  kModeAttendOnly = 2,  // gather and merge, using the partials of a previous select launch
+  kModeDense = 3        // exact attention over every block, no compensation
+};
 
 // Problem shape as the kernels see it.
 struct Shape {
   int B, Hq, Hkv, G, D, bs, r, P, max_blocks;
   int kmax;      // selected-block capacity per (sequence, KV head)
   int n_chunks;  // scan workgroups per (sequence, KV head)
+  int n_slices;  // first-level select workgroups per (sequence, KV head)
   int n_splits;  // gather workgroups per (sequence, KV head)
+  int pages_per_split;
   int dtype;     // 0 = bf16, 1 = f32
   float tau;     // 1 / sqrt(d)
   float tau2;    // 1 / d
@@ -31,11 +45,14 @@ struct Shape {
 
 // Device pointers carved from the caller's workspace.
 struct Work {
-  float* comp;  // [B][Hkv][n_chunks][G][D+4]   scan partials over all blocks: max s_bar, sum n e^{s_bar},
-                //                                sum n e^{s_bar}(1 + var_hat/2), sum n e^{s_bar} mean_v
-  float* lam;   // [B][Hq][max_blocks]          log of each block's per-head ranked score
-  float* gath;  // [B][Hkv][n_splits][G][2][D+4] gather partials: exact tokens, and the
-                //                                selected blocks' own compensation terms
+  uint32_t* ctrl;  // [kCtrlHeader + 4 * B * Hkv]: ticket, done, error, ...; per (b, g):
+                   //   scan-A arrivals, select arrivals, selection-ready flag, merge arrivals
+  float* xs;       // [B][Hq][max_blocks]  exp(log score - chunk max of log score)
+  float* cpart;    // [B][Hkv][n_chunks][G][D+4]  per chunk and head: max s_bar, sum w,
+                   //   sum w (1 + var_hat/2), max log score, sum w mean_v; w = n e^{s_bar - max}
+  uint64_t* cand;  // [B][Hkv][n_slices][kmax] first-level top-k candidates
+  float* gpart;    // [B][Hkv][n_splits][G][2][D+4] exact-token partials and the selected
+                   //   blocks' own compensation terms
 };
 
 struct Summ {
@@ -45,27 +62,27 @@ struct Summ {
   int32_t* count;
 };
 
+struct StepIO {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  Summ summ;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t* selected;
+  int32_t* num_selected;
+  float* group_scores;
+  float* out;
+  float* lse;
+  int score_mode;
+  int compensate;
+};
+
 hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   int append_only, const Summ& out, hipStream_t stream);
 
-hipError_t launch_scan(const Shape& s, const void* q, const Summ& summ, const int32_t* block_table,
-                       const int32_t* seq_lens, int score_mode, const Work& w, hipStream_t stream);
-
-hipError_t launch_select(const Shape& s, const int32_t* seq_lens, const Work& w, int32_t* selected,
-                         int32_t* num_selected, float* group_scores, hipStream_t stream);
-
-hipError_t launch_gather(const Shape& s, const void* q, const void* k_cache, const void* v_cache,
-                         const Summ& summ, const int32_t* block_table, const int32_t* seq_lens,
-                         const int32_t* selected, const int32_t* num_selected, int compensate,
-                         const Work& w, hipStream_t stream);
-
-hipError_t launch_merge(const Shape& s, const int32_t* seq_lens, const int32_t* num_selected,
-                        int compensate, const Work& w, float* out, float* lse, hipStream_t stream);
-
-// Dense: every block, no compensation.  `part` is [B][Hkv][n_splits][G][D+4].
-hipError_t launch_dense(const Shape& s, const void* q, const void* k_cache, const void* v_cache,
-                        const int32_t* block_table, const int32_t* seq_lens, float* part,
-                        float* out, float* lse, hipStream_t stream);
+// One launch of the decode-step kernel in the given mode.
+hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w, hipStream_t stream);
 
 }  // namespace ckv

@@ -128,10 +128,16 @@ ckv_status ckv_build_summaries(const ckv_dims* dims, const void* k_cache, const 
                                int32_t append_only, const ckv_summaries* summaries,
                                void* stream);
 
-/* Bytes of device workspace that ckv_score_select and
- * ckv_compensated_decode_attention need for these dims and this budget
- * (0 when dims are invalid).  The same workspace must be passed to both
- * calls of one decode step. */
+/* Bytes of device workspace that ckv_score_select,
+ * ckv_compensated_decode_attention and ckv_decode_step need for these dims
+ * and this budget (0 when dims are invalid).  The same workspace must be
+ * passed to both calls of one decode step.
+ * The workspace must be zero-filled before its first use: its first
+ * 64 + 4 * B * Hkv uint32 words are the step kernel's control words (work
+ * tickets and per-(sequence, KV head) arrival counters), which every call
+ * returns to zero.  Word 2 is an error flag that a call sets, and leaves
+ * set, if one of its bounded waits ever ran out (results are then
+ * unspecified).  Calls that share a workspace must not overlap. */
 size_t ckv_workspace_bytes(const ckv_dims* dims, int32_t budget_tokens);
 
 /* Score every block and select the top-k per (sequence, KV head) under a
@@ -188,7 +194,8 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
 
 /* Dense decode attention over every token (the baseline the method is
  * measured against: review "Summary", speed-up over full attention).
- * Workspace from ckv_dense_workspace_bytes.  lse may be NULL. */
+ * Workspace from ckv_dense_workspace_bytes, zero-filled before first use
+ * (same control words as above).  lse may be NULL. */
 size_t ckv_dense_workspace_bytes(const ckv_dims* dims);
 ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_table,

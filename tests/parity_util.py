@@ -2,9 +2,11 @@
 the same generated inputs, and compare them.
 
 Tolerances:
-  summaries  mean key / mean value: within 1 unit in the last place of the
-             KV dtype (bf16: the GPU accumulates in fp32, then rounds; the
-             oracle rounds the exact mean once); f32 storage: 2e-6 relative.
+  summaries  mean key / mean value: the GPU forms k0 + (sum_t (k_t - k0)) / n
+             in fp32, so per channel its error before storage is at most
+             (n + 2) 2^-24 (max_t |k_t - k0| + |mean|); the test allows twice
+             that, plus (bf16 storage) one unit in the last place of the
+             stored value.  Near a mean close to zero the first term dominates.
              grouped variance: 1e-5 relative (fp32 two-pass sums of <= 16
              terms, then a mean over <= 128 channels).
   selection  block ids bit-exact.  (a) against a CPU top-k of the GPU's own
@@ -69,6 +71,9 @@ def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.S
                                                   dev.block_table, dev.seq_lens, budget, sel, nsel, ws,
                                                   compensate=compensate)
     torch.cuda.synchronize()
+    ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
+    assert int(ctrl[2]) == 0, "a bounded wait in the step kernel ran out"
+    assert int(ctrl.abs().sum()) == 0, f"control words not reset: {ctrl.nonzero().flatten().tolist()}"
     return GpuResult(torch_to_storage(summaries.mean_k), torch_to_storage(summaries.mean_v),
                      summaries.gvar.cpu().numpy(), summaries.count.cpu().numpy(),
                      sel.cpu().numpy(), nsel.cpu().numpy(),
@@ -121,13 +126,22 @@ def check_summaries(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]
         pages = w.block_table[b, :M]
         gk, gv_, gg, gc = g.mean_k[pages], g.mean_v[pages], g.gvar[pages], g.count[pages]
         np.testing.assert_array_equal(gc, o.summ.count, err_msg=f"count seq {b}")
-        if w.dtype == "bf16":
-            for name, gpu, ref in (("mean_k", gk, o.summ.mean_k), ("mean_v", gv_, o.summ.mean_v)):
-                d = np.abs(_ordered_bf16(gpu) - _ordered_bf16(_oracle_bf16_bits(ref)))
-                assert d.max() <= 1, f"{name} seq {b}: {d.max()} bf16 ulps apart"
-        else:
-            np.testing.assert_allclose(gk, o.summ.mean_k, rtol=2e-6, atol=2e-6, err_msg=f"mean_k seq {b}")
-            np.testing.assert_allclose(gv_, o.summ.mean_v, rtol=2e-6, atol=2e-6, err_msg=f"mean_v seq {b}")
+        for name, gpu, tok in (("mean_k", gk, o.k), ("mean_v", gv_, o.v)):
+            ref = o.summ.mean_k if name == "mean_k" else o.summ.mean_v
+            gval = gpu.astype(np.float64) if w.dtype == "f32" else \
+                (gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            for i in range(M):
+                blk = tok[i * w.block_size:(i + 1) * w.block_size]
+                n = blk.shape[0]
+                spread = np.abs(blk - blk[0][None]).max(axis=0)
+                # fp32 accumulation error of k0 + sum(k - k0) / n, doubled ...
+                bound = 2 * (n + 2) * 2.0 ** -24 * (spread + np.abs(ref[i]))
+                if w.dtype == "bf16":
+                    # ... plus one unit in the last place of the stored bf16 value
+                    mag = np.maximum(np.abs(ref[i]), 2.0 ** -126)
+                    bound = bound + 2.0 ** (np.floor(np.log2(mag)) - 7)
+                err = np.abs(gval[i] - ref[i])
+                assert np.all(err <= bound), f"{name} seq {b} block {i}: {err.max()} > bound"
         np.testing.assert_allclose(gg, o.summ.gvar, rtol=1e-5, atol=1e-7, err_msg=f"gvar seq {b}")
 
 

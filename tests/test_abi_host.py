@@ -156,18 +156,20 @@ def test_workspace_checked(lib):
 
 
 def test_workspace_size_formula(lib):
-    # scan partials + per-head log scores + gather partials, each 256-byte aligned
+    # control words, per-block scores, scan partials, select candidates,
+    # gather partials; each region 256-byte aligned
     d = good_dims()
     def up(x):
         return (x + 255) // 256 * 256
-    n_chunks = (8192 + 255) // 256
+    n_chunks, n_slices = 8192 // 256, 8192 // 1024
+    ctrl = up((64 + 4 * 8) * 4)
     for budget in (0, 15, 16, 512, 2048, 10 ** 9):
         kmax = min(8192, budget // 16)
-        n_splits = (kmax + 3) // 4
-        expect = (up(1 * 8 * n_chunks * 4 * 132 * 4) + up(1 * 32 * 8192 * 4)
-                  + up(1 * 8 * n_splits * 4 * 2 * 132 * 4))
-        assert ws_bytes(lib, d, budget) == expect
-    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == up(8 * 256 * 4 * 132 * 4)
+        n_splits = min(64, max(1, (kmax + 3) // 4))
+        expect = (ctrl + up(32 * 8192 * 4) + up(8 * n_chunks * 4 * 132 * 4)
+                  + up(8 * n_slices * max(kmax, 1) * 8) + up(8 * n_splits * 4 * 2 * 132 * 4))
+        assert ws_bytes(lib, d, budget) == expect, budget
+    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + up(8 * 256 * 4 * 132 * 4)
 
 
 def test_errors_leave_no_stale_message_after_success_path_text(lib):

@@ -167,6 +167,27 @@ def test_append_matches_bulk_bit_exact():
     check_outputs(full, g, ora)
 
 
+def test_many_fused_steps_on_one_workspace():
+    # The step kernel's control words reset themselves: 25 launches in a row on
+    # one workspace give identical results and leave the words at zero.
+    w = small_gqa(seed=14)
+    dev = to_device(w)
+    dims = dev.dims
+    summ = C.allocate_summaries(dims, "cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
+    ws = C.allocate_workspace(C.workspace_bytes(dims, w.budget_tokens), "cuda:0")
+    outs = []
+    for _ in range(25):
+        sel, nsel, out, lse = C.decode_step(dims, dev.q, dev.k_cache, dev.v_cache, summ, dev.block_table,
+                                            dev.seq_lens, w.budget_tokens, ws)
+        outs.append((sel.clone(), out.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    for sel, out, lse in outs[1:]:
+        assert torch.equal(sel, outs[0][0]) and torch.equal(out, outs[0][1]) and torch.equal(lse, outs[0][2])
+    ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
+    assert int(ctrl.abs().sum()) == 0
+
+
 def test_repeat_runs_are_bit_identical():
     w = small_gqa(seed=13)
     a = run_gpu(w)
