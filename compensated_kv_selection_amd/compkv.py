@@ -130,10 +130,11 @@ class Dims:
 
 @dataclasses.dataclass
 class Summaries:
-    mean_k: torch.Tensor  # [P, Hkv, d] kv dtype
-    mean_v: torch.Tensor  # [P, Hkv, d] kv dtype
-    gvar: torch.Tensor    # [P, Hkv, r] float32
-    count: torch.Tensor   # [P] int32
+    """Block summaries by (sequence, KV head, logical block)."""
+    mean_k: torch.Tensor  # [B, Hkv, max_blocks, d] kv dtype
+    mean_v: torch.Tensor  # [B, Hkv, max_blocks, d] kv dtype
+    gvar: torch.Tensor    # [B, Hkv, max_blocks, r] float32
+    count: torch.Tensor   # [B, max_blocks] int32
 
     def c(self) -> CkvSummaries:
         return CkvSummaries(self.mean_k.data_ptr(), self.mean_v.data_ptr(),
@@ -141,11 +142,12 @@ class Summaries:
 
 
 def allocate_summaries(dims: Dims, device) -> Summaries:
-    P, H, d, r = dims.num_pages, dims.num_kv_heads, dims.head_dim, dims.r_groups
-    return Summaries(torch.zeros((P, H, d), dtype=dims.torch_dtype, device=device),
-                     torch.zeros((P, H, d), dtype=dims.torch_dtype, device=device),
-                     torch.zeros((P, H, r), dtype=torch.float32, device=device),
-                     torch.zeros((P,), dtype=torch.int32, device=device))
+    B, H, M = dims.batch, dims.num_kv_heads, dims.max_blocks_per_seq
+    d, r = dims.head_dim, dims.r_groups
+    return Summaries(torch.zeros((B, H, M, d), dtype=dims.torch_dtype, device=device),
+                     torch.zeros((B, H, M, d), dtype=dims.torch_dtype, device=device),
+                     torch.zeros((B, H, M, r), dtype=torch.float32, device=device),
+                     torch.zeros((B, M), dtype=torch.int32, device=device))
 
 
 def build_summaries(dims: Dims, k_cache, v_cache, block_table, seq_lens, summaries: Summaries,

@@ -72,6 +72,7 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.kmax = kb < x.max_blocks ? kb : x.max_blocks;
   x.n_chunks = (x.max_blocks + ckv::kChunk - 1) / ckv::kChunk;
   x.n_slices = (x.max_blocks + ckv::kSlice - 1) / ckv::kSlice;
+  x.share = x.kmax > 0 ? (x.kmax + x.n_slices - 1) / x.n_slices : 1;
   int splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
   splits = splits < 1 ? 1 : (splits > ckv::kMaxSplits ? ckv::kMaxSplits : splits);
   x.n_splits = splits;
@@ -79,7 +80,8 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.dtype = d->kv_dtype;
   x.tau = (float)(1.0 / sqrt((double)d->head_dim));
   x.tau2 = (float)(1.0 / (double)d->head_dim);
-  if (G * (x.n_chunks + 2 * x.n_splits) > ckv::kMergeFactors)
+  const int parts = x.n_slices > x.n_splits ? x.n_slices : x.n_splits;
+  if (G * (x.n_chunks + 2 * parts) > ckv::kMergeFactors)
     return fail(CKV_ERR_UNSUPPORTED, "too many partials for the merge");
   return CKV_OK;
 }
@@ -108,7 +110,8 @@ Layout layout(const ckv::Shape& s) {
   L.cand = off;
   off += align_up(bg * s.n_slices * (size_t)(s.kmax > 0 ? s.kmax : 1) * sizeof(uint64_t));
   L.gpart = off;
-  off += align_up(bg * s.n_splits * s.G * 2 * pst * sizeof(float));
+  const size_t parts = s.n_slices > s.n_splits ? s.n_slices : s.n_splits;
+  off += align_up(bg * parts * s.G * 2 * pst * sizeof(float));
   L.total = off;
   return L;
 }
@@ -218,9 +221,11 @@ ckv_status ckv_score_select(const ckv_dims* dims, const void* q, const ckv_summa
   CKV_TRY(check_workspace(s, workspace, workspace_bytes));
   ckv::StepIO io{q, nullptr, nullptr, to_summ(summaries), block_table, seq_lens, selected,
                  num_selected, group_scores, nullptr, nullptr, score_mode, 1};
-  return hip_status(ckv::launch_step(s, ckv::kModeSelectOnly, io, carve(s, workspace),
-                                     static_cast<hipStream_t>(stream)),
-                    "score/select launch");
+  const ckv::Work w = carve(s, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
+  if (e != hipSuccess) return hip_status(e, "scan launch");
+  return hip_status(ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st), "select launch");
 }
 
 ckv_status ckv_compensated_decode_attention(const ckv_dims* dims, const void* q,
@@ -269,9 +274,17 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
   CKV_TRY(check_workspace(s, workspace, workspace_bytes));
   ckv::StepIO io{q, k_cache, v_cache, to_summ(summaries), block_table, seq_lens, selected,
                  num_selected, nullptr, out, lse, score_mode, 1};
-  return hip_status(ckv::launch_step(s, ckv::kModeFused, io, carve(s, workspace),
-                                     static_cast<hipStream_t>(stream)),
-                    "decode step launch");
+  const ckv::Work w = carve(s, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // One launch when the workgroups that wait in it are few enough to leave
+  // free slots for those they wait on; otherwise three launches that never wait.
+  if (s.share <= ckv::kShareMax &&
+      2 * ckv::waiting_workgroups(s, ckv::kModeFused) < ckv::resident_workgroups(s, ckv::kModeFused))
+    return hip_status(ckv::launch_step(s, ckv::kModeFused, io, w, st), "decode step launch");
+  hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
+  if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
+  if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
+  return hip_status(e, "decode step launches");
 }
 
 size_t ckv_dense_workspace_bytes(const ckv_dims* dims) {

@@ -10,13 +10,15 @@ namespace ckv {
 
 constexpr int kBlockSize = 16;      // tokens per block = tokens per page
 constexpr int kChunk = 256;         // blocks scored by one scan workgroup
-constexpr int kSlice = 1024;        // blocks ranked by one first-level select workgroup
-constexpr int kGatherPages = 4;     // selected blocks per gather workgroup (grows past 64 splits)
-constexpr int kMaxSplits = 64;      // gather workgroups per (sequence, KV head), sparse step
+constexpr int kSlice = 1024;        // blocks ranked by one select workgroup
+constexpr int kGatherPages = 4;     // selected blocks per gather workgroup (unfused path)
+constexpr int kMaxSplits = 64;      // gather workgroups per (sequence, KV head), unfused path
 constexpr int kDensePages = 32;     // blocks per dense workgroup
 constexpr int kMaxBlocks = 15872;   // blocks per sequence (page-table width)
 constexpr int kMaxKvHeads = 64;
-constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks + 2 * splits)
+constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks + 2 * parts)
+constexpr int kCandLds = 2048;      // second-level candidates kept in LDS (else read from memory)
+constexpr int kShareMax = 256;      // selected blocks one select workgroup attends to (fused path)
 constexpr int kPartStride(int d) { return d + 4; }  // [m, l, z, c, acc[d]]
 constexpr int kCtrlHeader = 64;     // uint32 words before the per-(sequence, KV head) counters
 
@@ -24,42 +26,44 @@ enum ScoreMode { kScoreCompKV = 0, kScoreMass = 1 };
 
 // What one launch of the step kernel does.
 enum StepMode {
-  kModeFused = 0,       // score, select, gather, merge in one launch
-  kModeSelectOnly = 1,  // score and select; compensation partials stay in the workspace
-  kModeAttendOnly = 2,  // gather and merge, using the partials of a previous select launch
-  kModeDense = 3        // exact attention over every block, no compensation
+  kModeFused = 0,       // score, select, gather and merge in one launch
+  kModeScanOnly = 1,    // score every block; scores and compensation partials stay in the workspace
+  kModeSelectOnly = 2,  // top-k from the scores of a previous scan launch
+  kModeAttendOnly = 3,  // gather and merge, using the partials of previous scan/select launches
+  kModeDense = 4        // exact attention over every block, no compensation
 };
 
 // Problem shape as the kernels see it.
 struct Shape {
   int B, Hq, Hkv, G, D, bs, r, P, max_blocks;
-  int kmax;      // selected-block capacity per (sequence, KV head)
-  int n_chunks;  // scan workgroups per (sequence, KV head)
-  int n_slices;  // first-level select workgroups per (sequence, KV head)
-  int n_splits;  // gather workgroups per (sequence, KV head)
+  int kmax;           // selected-block capacity per (sequence, KV head)
+  int n_chunks;       // scan workgroups per (sequence, KV head)
+  int n_slices;       // select workgroups per (sequence, KV head)
+  int share;          // selected blocks attended by one select workgroup (fused)
+  int n_splits;       // gather workgroups per (sequence, KV head) (attend-only, dense)
   int pages_per_split;
-  int dtype;     // 0 = bf16, 1 = f32
-  float tau;     // 1 / sqrt(d)
-  float tau2;    // 1 / d
+  int dtype;          // 0 = bf16, 1 = f32
+  float tau;          // 1 / sqrt(d)
+  float tau2;         // 1 / d
 };
 
 // Device pointers carved from the caller's workspace.
 struct Work {
-  uint32_t* ctrl;  // [kCtrlHeader + 4 * B * Hkv]: ticket, done, error, ...; per (b, g):
-                   //   scan-A arrivals, select arrivals, selection-ready flag, merge arrivals
+  uint32_t* ctrl;  // [kCtrlHeader + 4 * B * Hkv]: error flag at 2; per (b, g): scan-A
+                   //   arrivals, select arrivals, merge arrivals, (spare)
   float* xs;       // [B][Hq][max_blocks]  exp(log score - chunk max of log score)
   float* cpart;    // [B][Hkv][n_chunks][G][D+4]  per chunk and head: max s_bar, sum w,
                    //   sum w (1 + var_hat/2), max log score, sum w mean_v; w = n e^{s_bar - max}
   uint64_t* cand;  // [B][Hkv][n_slices][kmax] first-level top-k candidates
-  float* gpart;    // [B][Hkv][n_splits][G][2][D+4] exact-token partials and the selected
-                   //   blocks' own compensation terms
+  float* gpart;    // [B][Hkv][n_parts][G][2][D+4] exact-token partials and the selected
+                   //   blocks' own compensation terms (n_parts = n_slices fused, else n_splits)
 };
 
 struct Summ {
-  void* mean_k;
-  void* mean_v;
-  float* gvar;
-  int32_t* count;
+  void* mean_k;   // [B][Hkv][max_blocks][D]
+  void* mean_v;   // [B][Hkv][max_blocks][D]
+  float* gvar;    // [B][Hkv][max_blocks][r]
+  int32_t* count; // [B][max_blocks]
 };
 
 struct StepIO {
@@ -81,6 +85,11 @@ struct StepIO {
 hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   int append_only, const Summ& out, hipStream_t stream);
+
+// Number of step-kernel workgroups that may wait on others in a launch of
+// this mode, and how many workgroups of the kernel fit on the device at once.
+int waiting_workgroups(const Shape& s, int mode);
+int resident_workgroups(const Shape& s, int mode);
 
 // One launch of the decode-step kernel in the given mode.
 hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w, hipStream_t stream);

@@ -51,10 +51,10 @@
  *   v_cache     [P][Hkv][block_size][d]    kv_dtype
  *   block_table [B][max_blocks_per_seq]    int32     logical block -> page
  *   seq_lens    [B]                        int32     tokens per sequence
- *   mean_k      [P][Hkv][d]                kv_dtype  (summaries are indexed by page)
- *   mean_v      [P][Hkv][d]                kv_dtype
- *   gvar        [P][Hkv][r]                float32
- *   count       [P]                        int32
+ *   mean_k      [B][Hkv][max_blocks][d]    kv_dtype  (summaries by logical block)
+ *   mean_v      [B][Hkv][max_blocks][d]    kv_dtype
+ *   gvar        [B][Hkv][max_blocks][r]    float32
+ *   count       [B][max_blocks]            int32
  *   selected    [B][Hkv][k_max]            int32, k_max = min(max_blocks_per_seq, budget/block_size)
  *   out         [B][Hq][d]                 float32
  *   lse         [B][Hq]                    float32 (natural log)
@@ -104,12 +104,15 @@ typedef struct {
   int32_t kv_dtype;           /* ckv_dtype of q, k_cache, v_cache, mean_k, mean_v */
 } ckv_dims;
 
+/* The summary store is indexed by (sequence, KV head, logical block), head
+ * major, so that scoring one KV head of one sequence streams contiguous
+ * memory; the keys and values themselves stay in the paged cache. */
 typedef struct {
-  void* mean_k;   /* [P][Hkv][d] kv_dtype: mean key of the page's tokens */
-  void* mean_v;   /* [P][Hkv][d] kv_dtype: mean value */
-  float* gvar;    /* [P][Hkv][r]: per channel group, the mean of the channels'
-                     population variances of the keys */
-  int32_t* count; /* [P]: tokens in the page */
+  void* mean_k;   /* [B][Hkv][max_blocks][d] kv_dtype: mean key of the block's tokens */
+  void* mean_v;   /* [B][Hkv][max_blocks][d] kv_dtype: mean value */
+  float* gvar;    /* [B][Hkv][max_blocks][r]: per channel group, the mean of the
+                     channels' population variances of the keys */
+  int32_t* count; /* [B][max_blocks]: tokens in the block */
 } ckv_summaries;
 
 /* Build block summaries from the paged cache (review "Summary", FAQ).
@@ -120,7 +123,7 @@ typedef struct {
  *   from its raw tokens, so bulk and append give identical bits.
  * Means are accumulated in float32 and rounded to kv_dtype (nearest, ties to
  * even); variances are two-pass (population, divide by n) in float32.
- * Summaries of pages not touched are left unchanged.
+ * Entries of blocks not touched are left unchanged.
  * Errors: CKV_ERR_INVALID_ARG / CKV_ERR_UNSUPPORTED for bad dims or null
  * pointers (nothing enqueued); CKV_ERR_HIP if the launch fails. */
 ckv_status ckv_build_summaries(const ckv_dims* dims, const void* k_cache, const void* v_cache,

@@ -37,10 +37,10 @@ LSE_ATOL = 1e-4
 
 @dataclasses.dataclass
 class GpuResult:
-    mean_k: np.ndarray   # storage dtype, [P, Hkv, d]
+    mean_k: np.ndarray   # storage dtype, [B, Hkv, max_blocks, d]
     mean_v: np.ndarray
-    gvar: np.ndarray
-    count: np.ndarray
+    gvar: np.ndarray     # [B, Hkv, max_blocks, r]
+    count: np.ndarray    # [B, max_blocks]
     selected: np.ndarray     # [B, Hkv, kmax]
     num_selected: np.ndarray  # [B, Hkv]
     group_scores: Optional[np.ndarray]  # [B, Hkv, max_blocks] float32
@@ -123,8 +123,10 @@ def check_summaries(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]
         if o is None:
             continue
         M = w.num_blocks(b)
-        pages = w.block_table[b, :M]
-        gk, gv_, gg, gc = g.mean_k[pages], g.mean_v[pages], g.gvar[pages], g.count[pages]
+        gk = g.mean_k[b, :, :M].transpose(1, 0, 2)   # -> [M, Hkv, d], the oracle's order
+        gv_ = g.mean_v[b, :, :M].transpose(1, 0, 2)
+        gg = g.gvar[b, :, :M].transpose(1, 0, 2)
+        gc = g.count[b, :M]
         np.testing.assert_array_equal(gc, o.summ.count, err_msg=f"count seq {b}")
         for name, gpu, tok in (("mean_k", gk, o.k), ("mean_v", gv_, o.v)):
             ref = o.summ.mean_k if name == "mean_k" else o.summ.mean_v

@@ -166,8 +166,9 @@ def test_workspace_size_formula(lib):
     for budget in (0, 15, 16, 512, 2048, 10 ** 9):
         kmax = min(8192, budget // 16)
         n_splits = min(64, max(1, (kmax + 3) // 4))
+        parts = max(n_slices, n_splits)   # gather partials: per slice (fused) or per split
         expect = (ctrl + up(32 * 8192 * 4) + up(8 * n_chunks * 4 * 132 * 4)
-                  + up(8 * n_slices * max(kmax, 1) * 8) + up(8 * n_splits * 4 * 2 * 132 * 4))
+                  + up(8 * n_slices * max(kmax, 1) * 8) + up(8 * parts * 4 * 2 * 132 * 4))
         assert ws_bytes(lib, d, budget) == expect, budget
     assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + up(8 * 256 * 4 * 132 * 4)
 

@@ -88,12 +88,14 @@ def test_mass_score_mode(budget):
 
 
 def test_fused_step_matches():
+    # One launch and the three-launch path select the same blocks; they split
+    # the exact attention differently, so outputs agree to rounding.
     w = small_gqa(seed=6)
     g1, _ = full_check(w)
     g2 = run_gpu(w, fused=True)
     np.testing.assert_array_equal(g1.selected, g2.selected)
-    np.testing.assert_array_equal(g1.out, g2.out)
-    np.testing.assert_array_equal(g1.lse, g2.lse)
+    np.testing.assert_allclose(g1.out, g2.out, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(g1.lse, g2.lse, rtol=1e-6, atol=1e-6)
 
 
 def test_constant_key_blocks_give_dense_output():
@@ -156,10 +158,10 @@ def test_append_matches_bulk_bit_exact():
         C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, lens, inc, append_only=True)
     torch.cuda.synchronize()
     for b in range(3):
-        pages = torch.from_numpy(full.block_table[b, :full.num_blocks(b)]).long().cuda()
+        M = full.num_blocks(b)
         for name in ("mean_k", "mean_v", "gvar"):
-            assert torch.equal(getattr(bulk, name)[pages], getattr(inc, name)[pages]), name
-        assert torch.equal(bulk.count[pages], inc.count[pages])
+            assert torch.equal(getattr(bulk, name)[b, :, :M], getattr(inc, name)[b, :, :M]), name
+        assert torch.equal(bulk.count[b, :M], inc.count[b, :M])
     g = run_gpu(full, dev=dev, summaries=inc)
     ora = run_oracle(full)
     check_summaries(full, g, ora)
@@ -269,5 +271,4 @@ def test_prefill_then_decode_loop():
             assert np.abs(out.cpu().numpy()[0] - o2).max() <= 2e-3
             assert np.abs(lse.cpu().numpy()[0] - l2).max() <= 1e-4
             M = -(-(L + 1) // 16)
-            page = int(w.block_table[0, M - 1])
-            assert summ.count[page].item() == osumm.count[M - 1]
+            assert summ.count[0, M - 1].item() == osumm.count[M - 1]
