@@ -20,7 +20,7 @@ LIB_NAME = "libcompkv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kernels.hip", "abi.cpp"]
+SOURCES = ["kernels.hip", "fused.hip", "abi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -72,7 +72,8 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.kmax = kb < x.max_blocks ? kb : x.max_blocks;
   x.n_chunks = (x.max_blocks + ckv::kChunk - 1) / ckv::kChunk;
   x.n_slices = (x.max_blocks + ckv::kSlice - 1) / ckv::kSlice;
-  x.share = x.kmax > 0 ? (x.kmax + x.n_slices - 1) / x.n_slices : 1;
+  x.share = x.kmax > 0 ? (x.kmax + x.n_chunks - 1) / x.n_chunks : 1;
+  x.bg_round = 0;
   int splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
   splits = splits < 1 ? 1 : (splits > ckv::kMaxSplits ? ckv::kMaxSplits : splits);
   x.n_splits = splits;
@@ -80,26 +81,27 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.dtype = d->kv_dtype;
   x.tau = (float)(1.0 / sqrt((double)d->head_dim));
   x.tau2 = (float)(1.0 / (double)d->head_dim);
-  const int parts = x.n_slices > x.n_splits ? x.n_slices : x.n_splits;
-  if (G * (x.n_chunks + 2 * parts) > ckv::kMergeFactors)
+  if (G * (x.n_chunks + 2 * x.n_splits) > ckv::kMergeFactors)
     return fail(CKV_ERR_UNSUPPORTED, "too many partials for the merge");
   return CKV_OK;
 }
 
 struct Layout {
-  size_t ctrl, xs, cpart, cand, gpart, total;
+  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, total;
 };
 
 size_t ctrl_bytes(const ckv::Shape& s) {
   return align_up((size_t)(ckv::kCtrlHeader + 4 * s.B * s.Hkv) * sizeof(uint32_t));
 }
 
-// Sparse-step workspace: control words, per-block scores, scan partials,
-// first-level select candidates, gather partials.
+// Sparse-step workspace: control words, per-block scores, chunk partials,
+// first-level select candidates, gather partials, and the words the fused
+// step publishes (chunk headers and candidates; all zero between calls).
 Layout layout(const ckv::Shape& s) {
   Layout L;
   const size_t pst = ckv::kPartStride(s.D);
   const size_t bg = (size_t)s.B * s.Hkv;
+  const size_t kcap = (size_t)(s.kmax > 0 ? s.kmax : 1);
   size_t off = 0;
   L.ctrl = off;
   off += ctrl_bytes(s);
@@ -108,10 +110,13 @@ Layout layout(const ckv::Shape& s) {
   L.cpart = off;
   off += align_up(bg * s.n_chunks * s.G * pst * sizeof(float));
   L.cand = off;
-  off += align_up(bg * s.n_slices * (size_t)(s.kmax > 0 ? s.kmax : 1) * sizeof(uint64_t));
+  off += align_up(bg * s.n_slices * kcap * sizeof(uint64_t));
   L.gpart = off;
-  const size_t parts = s.n_slices > s.n_splits ? s.n_slices : s.n_splits;
-  off += align_up(bg * parts * s.G * 2 * pst * sizeof(float));
+  off += align_up(bg * s.n_splits * s.G * 2 * pst * sizeof(float));
+  L.fhdr = off;
+  off += align_up(bg * s.n_chunks * s.G * sizeof(uint64_t));
+  L.fcand = off;
+  off += align_up(bg * s.n_chunks * kcap * sizeof(uint64_t));
   L.total = off;
   return L;
 }
@@ -121,7 +126,8 @@ ckv::Work carve(const ckv::Shape& s, void* ws) {
   char* base = static_cast<char*>(ws);
   return ckv::Work{reinterpret_cast<uint32_t*>(base + L.ctrl), reinterpret_cast<float*>(base + L.xs),
                    reinterpret_cast<float*>(base + L.cpart), reinterpret_cast<uint64_t*>(base + L.cand),
-                   reinterpret_cast<float*>(base + L.gpart)};
+                   reinterpret_cast<float*>(base + L.gpart), reinterpret_cast<uint64_t*>(base + L.fhdr),
+                   reinterpret_cast<uint64_t*>(base + L.fcand)};
 }
 
 void set_dense(ckv::Shape& s) {
@@ -276,11 +282,16 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                  num_selected, nullptr, out, lse, score_mode, 1};
   const ckv::Work w = carve(s, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // One launch when the workgroups that wait in it are few enough to leave
-  // free slots for those they wait on; otherwise three launches that never wait.
-  if (s.share <= ckv::kShareMax &&
-      2 * ckv::waiting_workgroups(s, ckv::kModeFused) < ckv::resident_workgroups(s, ckv::kModeFused))
-    return hip_status(ckv::launch_step(s, ckv::kModeFused, io, w, st), "decode step launch");
+  // One launch when its whole grid - at least every chunk of one (sequence,
+  // KV head) pair - can be resident at once and the pair's candidates fit in
+  // shared memory; otherwise three launches that never wait.
+  const int resident = ckv::fused_resident_workgroups(s);
+  const int per_round = resident / s.n_chunks;
+  if (per_round >= 1 && s.share <= ckv::kShareMax && s.n_chunks * s.kmax <= ckv::kFusedCand) {
+    const int bgs = s.B * s.Hkv;
+    s.bg_round = per_round < bgs ? per_round : bgs;
+    return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
+  }
   hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
@@ -312,7 +323,7 @@ ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const
     return fail(CKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(workspace);
   ckv::Work w{reinterpret_cast<uint32_t*>(base), nullptr, nullptr, nullptr,
-              reinterpret_cast<float*>(base + ctrl_bytes(s))};
+              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr};
   ckv::StepIO io{q, k_cache, v_cache, ckv::Summ{nullptr, nullptr, nullptr, nullptr}, block_table,
                  seq_lens, nullptr, nullptr, nullptr, out, lse, 0, 0};
   return hip_status(ckv::launch_step(s, ckv::kModeDense, io, w, static_cast<hipStream_t>(stream)),

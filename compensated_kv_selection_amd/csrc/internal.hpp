@@ -18,7 +18,10 @@ constexpr int kMaxBlocks = 15872;   // blocks per sequence (page-table width)
 constexpr int kMaxKvHeads = 64;
 constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks + 2 * parts)
 constexpr int kCandLds = 2048;      // second-level candidates kept in LDS (else read from memory)
-constexpr int kShareMax = 256;      // selected blocks one select workgroup attends to (fused path)
+constexpr int kShareMax = 256;      // selected blocks one fused workgroup attends to
+constexpr int kMaxChunks = (kMaxBlocks + kChunk - 1) / kChunk;
+constexpr int kFusedThreads = 512;  // fused step: 4 control waves + 4 value waves
+constexpr int kFusedCand = 4608;    // fused step: candidates of all chunks held in LDS
 constexpr int kPartStride(int d) { return d + 4; }  // [m, l, z, c, acc[d]]
 constexpr int kCtrlHeader = 64;     // uint32 words before the per-(sequence, KV head) counters
 
@@ -39,7 +42,8 @@ struct Shape {
   int kmax;           // selected-block capacity per (sequence, KV head)
   int n_chunks;       // scan workgroups per (sequence, KV head)
   int n_slices;       // select workgroups per (sequence, KV head)
-  int share;          // selected blocks attended by one select workgroup (fused)
+  int share;          // selected blocks attended by one chunk workgroup (fused)
+  int bg_round;       // (sequence, KV head) pairs processed at once by the fused grid
   int n_splits;       // gather workgroups per (sequence, KV head) (attend-only, dense)
   int pages_per_split;
   int dtype;          // 0 = bf16, 1 = f32
@@ -55,8 +59,10 @@ struct Work {
   float* cpart;    // [B][Hkv][n_chunks][G][D+4]  per chunk and head: max s_bar, sum w,
                    //   sum w (1 + var_hat/2), max log score, sum w mean_v; w = n e^{s_bar - max}
   uint64_t* cand;  // [B][Hkv][n_slices][kmax] first-level top-k candidates
-  float* gpart;    // [B][Hkv][n_parts][G][2][D+4] exact-token partials and the selected
-                   //   blocks' own compensation terms (n_parts = n_slices fused, else n_splits)
+  float* gpart;    // [B][Hkv][n_splits][G][2][D+4] exact-token partials and the selected
+                   //   blocks' own compensation terms
+  uint64_t* fhdr;  // [B][Hkv][n_chunks][G] fused: chunk header (max s_bar, Z_hat part), 0 = unset
+  uint64_t* fcand; // [B][Hkv][n_chunks][kmax] fused: chunk candidates, 0 = unset
 };
 
 struct Summ {
@@ -86,12 +92,15 @@ hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const voi
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   int append_only, const Summ& out, hipStream_t stream);
 
-// Number of step-kernel workgroups that may wait on others in a launch of
-// this mode, and how many workgroups of the kernel fit on the device at once.
-int waiting_workgroups(const Shape& s, int mode);
-int resident_workgroups(const Shape& s, int mode);
-
-// One launch of the decode-step kernel in the given mode.
+// One launch of the decode-step kernel in the given mode (not kModeFused).
 hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w, hipStream_t stream);
+
+// Workgroups of the fused step kernel that fit on the current device at once
+// (0 if the kernel cannot run with this shape).
+int fused_resident_workgroups(const Shape& s);
+
+// One launch of the fused step kernel; s.bg_round must be set, with
+// s.bg_round * s.n_chunks <= fused_resident_workgroups(s).
+hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t stream);
 
 }  // namespace ckv

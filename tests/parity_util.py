@@ -29,6 +29,7 @@ from compensated_kv_selection_amd import compkv as C
 from compensated_kv_selection_amd.tensors import to_device, torch_to_storage
 from compensated_kv_selection_amd.workloads import DecodeInputs
 from oracle import compkv_oracle as O
+from ws_layout import workspace_regions
 
 NEAR_TIE = 1e-5
 OUT_ATOL = 2e-3
@@ -46,6 +47,19 @@ class GpuResult:
     group_scores: Optional[np.ndarray]  # [B, Hkv, max_blocks] float32
     out: np.ndarray          # [B, Hq, d]
     lse: np.ndarray          # [B, Hq]
+
+
+def check_workspace_clean(ws, dims, budget):
+    """Every call leaves the control words and the fused step's published
+    words (the last two workspace regions) zero, ready for the next call."""
+    ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
+    assert int(ctrl[2]) == 0, "a bounded wait in the step kernel ran out"
+    assert int(ctrl.abs().sum()) == 0, f"control words not reset: {ctrl.nonzero().flatten().tolist()}"
+    regions = workspace_regions(dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim,
+                                dims.max_blocks_per_seq, budget)
+    assert sum(regions) == ws.numel(), (sum(regions), ws.numel())
+    tail = ws[sum(regions[:-2]):].view(torch.int64).cpu()
+    assert int((tail != 0).sum()) == 0, "published words not cleared"
 
 
 def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.SCORE_COMPKV,
@@ -71,9 +85,7 @@ def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.S
                                                   dev.block_table, dev.seq_lens, budget, sel, nsel, ws,
                                                   compensate=compensate)
     torch.cuda.synchronize()
-    ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
-    assert int(ctrl[2]) == 0, "a bounded wait in the step kernel ran out"
-    assert int(ctrl.abs().sum()) == 0, f"control words not reset: {ctrl.nonzero().flatten().tolist()}"
+    check_workspace_clean(ws, dims, budget)
     return GpuResult(torch_to_storage(summaries.mean_k), torch_to_storage(summaries.mean_v),
                      summaries.gvar.cpu().numpy(), summaries.count.cpu().numpy(),
                      sel.cpu().numpy(), nsel.cpu().numpy(),

@@ -9,6 +9,7 @@ import re
 import pytest
 
 from compensated_kv_selection_amd import compkv as C
+from ws_layout import workspace_regions
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "compkv.h")
@@ -156,21 +157,12 @@ def test_workspace_checked(lib):
 
 
 def test_workspace_size_formula(lib):
-    # control words, per-block scores, scan partials, select candidates,
-    # gather partials; each region 256-byte aligned
     d = good_dims()
-    def up(x):
-        return (x + 255) // 256 * 256
-    n_chunks, n_slices = 8192 // 256, 8192 // 1024
-    ctrl = up((64 + 4 * 8) * 4)
     for budget in (0, 15, 16, 512, 2048, 10 ** 9):
-        kmax = min(8192, budget // 16)
-        n_splits = min(64, max(1, (kmax + 3) // 4))
-        parts = max(n_slices, n_splits)   # gather partials: per slice (fused) or per split
-        expect = (ctrl + up(32 * 8192 * 4) + up(8 * n_chunks * 4 * 132 * 4)
-                  + up(8 * n_slices * max(kmax, 1) * 8) + up(8 * parts * 4 * 2 * 132 * 4))
+        expect = sum(workspace_regions(1, 32, 8, 128, 8192, budget))
         assert ws_bytes(lib, d, budget) == expect, budget
-    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + up(8 * 256 * 4 * 132 * 4)
+    ctrl = workspace_regions(1, 32, 8, 128, 8192, 0)[0]
+    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + (8 * 256 * 4 * 132 * 4 + 255) // 256 * 256
 
 
 def test_errors_leave_no_stale_message_after_success_path_text(lib):

@@ -10,7 +10,7 @@ from compensated_kv_selection_amd.tensors import to_device
 from oracle import compkv_oracle as O
 
 from parity_util import (check_outputs, check_selection_isolated, check_selection_vs_oracle,
-                         check_summaries, run_gpu, run_oracle)
+                         check_summaries, check_workspace_clean, run_gpu, run_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,20 +23,31 @@ def _gpu():
     yield
 
 
-def full_check(w, budget=None, score_mode=C.SCORE_COMPKV, compensate=True, fused=False, report=None):
+def full_check(w, budget=None, score_mode=C.SCORE_COMPKV, compensate=True, fused=None, report=None):
+    """Run the case through the three-launch path (fused=False), the
+    single-launch step (fused=True) or both (None; the single-launch step
+    always compensates) and check each against the oracle."""
     budget = w.budget_tokens if budget is None else budget
-    print(f"[case] {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
-          f"d={w.head_dim} r={w.r_groups} {w.dtype} lens={list(w.seq_lens)[:6]} budget={budget} "
-          f"mode={score_mode} comp={compensate} fused={fused}", flush=True)
-    g = run_gpu(w, budget, score_mode, compensate, fused=fused)
-    ora = run_oracle(w, budget, score_mode, compensate)
-    check_summaries(w, g, ora)
-    if not fused:
-        check_selection_isolated(w, g, budget)
-    near = check_selection_vs_oracle(w, g, ora, report)
-    err = check_outputs(w, g, ora, compensate)
-    print(f"[case] ok: max |out - oracle| = {err:.2e}, near-ties {near}", flush=True)
-    return g, ora
+    ora = None
+    g_first = None
+    paths = [False, True] if fused is None else [fused]
+    if not compensate:
+        paths = [False]
+    for fz in paths:
+        print(f"[case] {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+              f"d={w.head_dim} r={w.r_groups} {w.dtype} lens={list(w.seq_lens)[:6]} budget={budget} "
+              f"mode={score_mode} comp={compensate} fused={fz}", flush=True)
+        g = run_gpu(w, budget, score_mode, compensate, fused=fz)
+        if ora is None:
+            ora = run_oracle(w, budget, score_mode, compensate)
+        check_summaries(w, g, ora)
+        if not fz:
+            check_selection_isolated(w, g, budget)
+        near = check_selection_vs_oracle(w, g, ora, report)
+        err = check_outputs(w, g, ora, compensate)
+        print(f"[case] ok: max |out - oracle| = {err:.2e}, near-ties {near}", flush=True)
+        g_first = g_first or g
+    return g_first, ora
 
 
 def small_gqa(seed=0, **kw):
@@ -91,7 +102,7 @@ def test_fused_step_matches():
     # One launch and the three-launch path select the same blocks; they split
     # the exact attention differently, so outputs agree to rounding.
     w = small_gqa(seed=6)
-    g1, _ = full_check(w)
+    g1, _ = full_check(w, fused=False)
     g2 = run_gpu(w, fused=True)
     np.testing.assert_array_equal(g1.selected, g2.selected)
     np.testing.assert_allclose(g1.out, g2.out, rtol=1e-5, atol=1e-6)
@@ -186,8 +197,7 @@ def test_many_fused_steps_on_one_workspace():
     torch.cuda.synchronize()
     for sel, out, lse in outs[1:]:
         assert torch.equal(sel, outs[0][0]) and torch.equal(out, outs[0][1]) and torch.equal(lse, outs[0][2])
-    ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
-    assert int(ctrl.abs().sum()) == 0
+    check_workspace_clean(ws, dims, w.budget_tokens)
 
 
 def test_repeat_runs_are_bit_identical():
@@ -212,7 +222,7 @@ def test_llama_128k_headline():
 
 
 def test_llama_128k_headline_unfused_scores():
-    full_check(W.make_preset("llama_128k", seed=1))
+    full_check(W.make_preset("llama_128k", seed=1), fused=False)
 
 
 def test_batched_ragged():

@@ -1,0 +1,21 @@
+"""Expected region sizes of the sparse-step workspace (what the C ABI's
+ckv_workspace_bytes must return, and where the fused step's published words
+lie)."""
+
+
+def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
+    """Region sizes of the sparse-step workspace, each 256-byte aligned:
+    control words, per-block scores, chunk partials, select candidates,
+    gather partials, fused chunk headers, fused candidates."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    G = Hq // Hkv
+    bg = B * Hkv
+    pst = D + 4
+    n_chunks, n_slices = -(-max_blocks // 256), -(-max_blocks // 1024)
+    kmax = min(max_blocks, budget // 16)
+    kcap = max(kmax, 1)
+    n_splits = min(64, max(1, (kmax + 3) // 4))
+    return [up((64 + 4 * bg) * 4), up(B * Hq * max_blocks * 4), up(bg * n_chunks * G * pst * 4),
+            up(bg * n_slices * kcap * 8), up(bg * n_splits * G * 2 * pst * 4),
+            up(bg * n_chunks * G * 8), up(bg * n_chunks * kcap * 8)]
