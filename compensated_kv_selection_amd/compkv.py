@@ -178,13 +178,16 @@ def allocate_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 CTRL_WORDS_HEADER = 64
+CTRL_WORDS_PER_PAIR = 8
+CTRL_EPOCH = 3   # per-pair word that counts single-launch steps
 
 
 def workspace_control(ws: torch.Tensor, batch: int, num_kv_heads: int) -> torch.Tensor:
-    """The workspace's control words as int32 (host copy): [ticket, done,
-    error flag, ...] then four counters per (sequence, KV head).  All are zero
-    between calls; the error flag is set if a bounded wait ever ran out."""
-    n = CTRL_WORDS_HEADER + 4 * batch * num_kv_heads
+    """The workspace's control words as int32 (host copy): 64 header words
+    (word 2: error flag) then eight words per (sequence, KV head).  Between
+    calls every word is zero except each pair's step counter (word 3 of the
+    pair); the error flag is set if a bounded wait ever ran out."""
+    n = CTRL_WORDS_HEADER + CTRL_WORDS_PER_PAIR * batch * num_kv_heads
     return ws[: 4 * n].view(torch.int32).cpu()
 
 

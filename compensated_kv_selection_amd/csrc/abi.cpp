@@ -87,16 +87,17 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
 }
 
 struct Layout {
-  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, total;
+  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, fw, fpart, total;
 };
 
 size_t ctrl_bytes(const ckv::Shape& s) {
-  return align_up((size_t)(ckv::kCtrlHeader + 4 * s.B * s.Hkv) * sizeof(uint32_t));
+  return align_up((size_t)(ckv::kCtrlHeader + ckv::kCtrlPerPair * s.B * s.Hkv) * sizeof(uint32_t));
 }
 
 // Sparse-step workspace: control words, per-block scores, chunk partials,
-// first-level select candidates, gather partials, and the words the fused
-// step publishes (chunk headers and candidates; all zero between calls).
+// first-level select candidates, gather partials, and what the fused step
+// hands between workgroups: chunk headers and candidates (zero between
+// calls), tagged compensation weights, and chunk partials.
 Layout layout(const ckv::Shape& s) {
   Layout L;
   const size_t pst = ckv::kPartStride(s.D);
@@ -117,6 +118,10 @@ Layout layout(const ckv::Shape& s) {
   off += align_up(bg * s.n_chunks * s.G * sizeof(uint64_t));
   L.fcand = off;
   off += align_up(bg * s.n_chunks * kcap * sizeof(uint64_t));
+  L.fw = off;
+  off += align_up(bg * s.n_chunks * s.G * (ckv::kChunk + 1) * sizeof(uint64_t));
+  L.fpart = off;
+  off += align_up(bg * 2 * s.n_chunks * s.G * (size_t)(s.D + 2) * sizeof(uint64_t));
   L.total = off;
   return L;
 }
@@ -127,7 +132,8 @@ ckv::Work carve(const ckv::Shape& s, void* ws) {
   return ckv::Work{reinterpret_cast<uint32_t*>(base + L.ctrl), reinterpret_cast<float*>(base + L.xs),
                    reinterpret_cast<float*>(base + L.cpart), reinterpret_cast<uint64_t*>(base + L.cand),
                    reinterpret_cast<float*>(base + L.gpart), reinterpret_cast<uint64_t*>(base + L.fhdr),
-                   reinterpret_cast<uint64_t*>(base + L.fcand)};
+                   reinterpret_cast<uint64_t*>(base + L.fcand), reinterpret_cast<uint64_t*>(base + L.fw),
+                   reinterpret_cast<uint64_t*>(base + L.fpart)};
 }
 
 void set_dense(ckv::Shape& s) {
@@ -282,11 +288,12 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                  num_selected, nullptr, out, lse, score_mode, 1};
   const ckv::Work w = carve(s, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // One launch when its whole grid - at least every chunk of one (sequence,
-  // KV head) pair - can be resident at once and the pair's candidates fit in
-  // shared memory; otherwise three launches that never wait.
+  // One launch when its whole grid - at least the two workgroups of every
+  // chunk of one (sequence, KV head) pair - can be resident at once and the
+  // pair's candidates fit in shared memory; otherwise three launches that
+  // never wait.
   const int resident = ckv::fused_resident_workgroups(s);
-  const int per_round = resident / s.n_chunks;
+  const int per_round = resident / (2 * s.n_chunks);
   if (per_round >= 1 && s.share <= ckv::kShareMax && s.n_chunks * s.kmax <= ckv::kFusedCand) {
     const int bgs = s.B * s.Hkv;
     s.bg_round = per_round < bgs ? per_round : bgs;
@@ -323,7 +330,7 @@ ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const
     return fail(CKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(workspace);
   ckv::Work w{reinterpret_cast<uint32_t*>(base), nullptr, nullptr, nullptr,
-              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr};
+              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr, nullptr, nullptr};
   ckv::StepIO io{q, k_cache, v_cache, ckv::Summ{nullptr, nullptr, nullptr, nullptr}, block_table,
                  seq_lens, nullptr, nullptr, nullptr, out, lse, 0, 0};
   return hip_status(ckv::launch_step(s, ckv::kModeDense, io, w, static_cast<hipStream_t>(stream)),

@@ -12,29 +12,36 @@
 // exactly; each omitted block enters the softmax once with weight
 // n e^{s_bar} and value mean_v.
 //
-// Organisation.  One workgroup per (sequence, KV head, chunk of 256 blocks).
-// The grid covers bg_round (sequence, KV head) pairs at once and walks the
-// rest in rounds; every workgroup of the grid is resident, so the workgroups
-// of a pair can wait for each other.  A workgroup has 8 waves:
-//   control waves 0-3 load the chunk's mean keys and grouped variances,
-//     compute the block-mean logits on the matrix cores (the G query heads
-//     are the rows of a 16x16x32 bf16 MFMA tile), publish the chunk header
-//     (max logit, partial Z_hat per head), read every header of the pair,
-//     rank the chunk's blocks, publish the chunk's top-k candidates, read
-//     every candidate of the pair, find the pair's top-k, and attend exactly
-//     to the workgroup's share of the selected blocks;
-//   value waves 4-7 stream the chunk's mean values from the start and, once
-//     the selection is known, sum the compensation terms of the chunk's
-//     omitted blocks.
-// A wave's memory counter drains in issue order, so a wave that waits for a
-// load waits for every load it issued before.  Value waves therefore never
-// read what other workgroups publish, and control waves never hold the
-// long mean-value stream.  Headers and candidates are 64-bit words that are
-// never 0 once written; readers poll them until nonzero, so publishing
-// needs no completion wait and no counter.  Each workgroup then publishes
-// one (max, sum, acc[d]) partial per query head and counts itself; the last
-// to arrive merges the pair's partials into the output and clears the pair's
-// headers and candidates, which leaves the workspace ready for the next call.
+// Organisation.  Every (sequence, KV head) pair is split into chunks of 256
+// blocks, and every chunk gets two workgroups of 4 waves:
+//   a control workgroup loads the chunk's mean keys, grouped variances and
+//     page-table entries, computes the block-mean logits on the matrix cores
+//     (the G query heads are the rows of a 16x16x32 bf16 MFMA tile),
+//     publishes the chunk's compensation weights and header (max logit,
+//     partial Z_hat per head), reads every header of the pair, ranks the
+//     chunk's blocks, publishes the chunk's top-k candidates, reads every
+//     candidate of the pair, finds the pair's top-k, attends exactly to the
+//     selected blocks that lie in its chunk and takes back their
+//     compensation terms;
+//   a value workgroup waits for the chunk's weights, streams the chunk's mean
+//     values and sums the compensation terms of all the chunk's blocks.
+// A wave's memory counter drains in issue order, so the long mean-value
+// stream lives in workgroups that never wait on small hand-offs, and it
+// starts once the mean keys have arrived, so that the ranking does not wait
+// behind it.
+// Hand-offs go through device-coherent (sc1) memory.  Headers and candidates
+// are 64-bit words that are never 0 once written (cleared after use);
+// weights and partials carry the call's epoch in their upper half.  Readers
+// poll such words directly, so publishing needs no completion wait.  Each
+// workgroup publishes one (max, sum, acc[d]) partial per query head, then
+// merges its slice of the pair's output from all the pair's partials; the
+// last to finish clears the pair's headers and candidates and advances its
+// epoch.
+//
+// The grid covers bg_round pairs at once and walks the rest in rounds; the
+// host launches it only when the whole grid can be resident, so the
+// workgroups of a pair can wait for each other.  Every wait is bounded and
+// sets the error word when it runs out.
 #include <type_traits>
 
 #include "step_common.hpp"
@@ -43,56 +50,80 @@ namespace ckv {
 
 namespace {
 
-constexpr int NT = kFusedThreads;  // threads per workgroup
-constexpr int NCTL = NT / 2;       // control threads
-constexpr int kPollBatch = 8;      // published words read per thread per round trip
-constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and call
+constexpr int NT = 256;                    // threads per workgroup
+constexpr int NW = NT / 64;                // waves per workgroup
+constexpr int kPollBatch = 8;              // published words read per thread per round trip
+constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
+constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
 
 template <int D, int G>
-struct FusedLds {
-  static constexpr int NW = NT / 64;
-  float qf[G * D];        // this KV head's query rows
+struct CtlLds {
+  static constexpr int CPR = D / 8;  // 16-byte pieces per mean-key row
+  float qf[NT * 8];       // this KV head's query rows (G * D), then zeros
   float qn[G * D];        // |q_h restricted to channel group t|^2, [G][r]
+  float qsq[NT];          // per-thread 8-channel partials of |q|^2
   float sb[G][kChunk];    // block-mean logit tau q.mean_k
   float lam[G][kChunk];   // estimated logit variance, then log of the per-head score
   float wt[G][kChunk];    // compensation weight n e^{s_bar - chunk max}
   float mx[G];            // chunk max of s_bar per head
   float lnz[G];           // log Z_hat per head
-  float hdr[kMaxChunks * G * 2];  // merge: (max, sum) of every partial
   union {
-    uint64_t keys[kFusedCand];    // headers, chunk keys, then the pair's candidates
-    float red[NW][G][D + 4];      // per-wave partial states
-    float fac[kMaxChunks * G];    // merge factors
+    uint64_t keys[kFusedCand];  // headers, chunk keys, then the pair's candidates
+    uint4 stage[NW][16 * CPR];  // mean-key rows in matrix-operand order, per wave
+    float red[NW][G][D + 4];    // per-wave partial states
   } u;
-  float mtot[G], ltot[G];
   uint32_t hist[512];
   uint32_t bitmap[kMaxBlocks / 32];
-  int blk[kShareMax];
-  int pg[kShareMax];
-  int nn[kShareMax];
-  uint32_t sh[4];
+  int pgt[kChunk];        // page of each block of the chunk
+  int own[kChunk];        // selected blocks of this chunk (local rows, ascending)
+  uint32_t sh[64];
   uint32_t wsum[NW];
   uint32_t count;
-  uint32_t slot;
 };
 
+template <int D, int G>
+struct ValLds {
+  float w[G][kChunk];
+  float mx[G];
+  float red[NW][G][D + 4];
+};
+
+template <int D, int G>
+struct MergeLds {
+  float pm[NT], pl[NT];
+  float4 pa[NT];
+};
+
+template <int D, int G>
+union FusedLds {
+  CtlLds<D, G> c;
+  ValLds<D, G> v;
+  MergeLds<D, G> m;
+};
+
+__device__ __forceinline__ uint32_t* ctr_epoch(const Work& w, int bg) { return w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 3; }
+__device__ __forceinline__ uint32_t* ctr_done(const Work& w, int bg) { return w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 5; }
+
+__device__ __forceinline__ uint64_t tagged(float x, uint32_t tag) {
+  return ((uint64_t)tag << 32) | __float_as_uint(x);
+}
+
 // Copy n published 64-bit words into dst, waiting for each to become
-// nonzero.  Word e is read at index (e / per) * stride + e % per.  Run by
-// the control threads; each thread's re-reads are bounded in total, and
-// running out sets the error word.
+// nonzero.  Word e is read at index (e / per) * stride + e % per.  Each
+// thread's re-reads are bounded in total; running out sets the error word.
 __device__ void read_published(const Coh& src, int n, int per, int stride, uint64_t* dst, uint32_t* err) {
   const int t = threadIdx.x;
   uint32_t spins = 0;
-  for (int base = 0; base < n; base += NCTL * kPollBatch) {
+  for (int base = 0; base < n; base += NT * kPollBatch) {
     uint64_t v[kPollBatch];
 #pragma unroll
     for (int u = 0; u < kPollBatch; ++u) {
-      const int e = base + t + u * NCTL;
+      const int e = base + t + u * NT;
       v[u] = e < n ? src.u64((e / per) * stride + e % per) : 1u;
     }
 #pragma unroll
     for (int u = 0; u < kPollBatch; ++u) {
-      const int e = base + t + u * NCTL;
+      const int e = base + t + u * NT;
       while (v[u] == 0 && spins < kPollLimit) {
         __builtin_amdgcn_s_sleep(1);
         v[u] = src.u64((e / per) * stride + e % per);
@@ -103,116 +134,188 @@ __device__ void read_published(const Coh& src, int n, int per, int stride, uint6
   }
 }
 
-// Returns true in the workgroup that arrived last for this pair.
+// Wait until word i of src carries this call's tag; returns its float.
+__device__ __forceinline__ float read_tagged(const Coh& src, int i, uint64_t v, uint32_t tag, uint32_t& spins,
+                                             uint32_t* err) {
+  while ((uint32_t)(v >> 32) != tag && spins < kPollLimit) {
+    __builtin_amdgcn_s_sleep(1);
+    v = src.u64(i);
+    if (++spins == kPollLimit) st_c(err, 1u);
+  }
+  return __uint_as_float((uint32_t)v);
+}
+
+// Per-thread attention state of G query heads -> one partial per head at
+// `part` ([G][D + 2] tagged words: max, sum, acc[D]), combining the row
+// slots of each wave with lane swaps, then the waves through LDS.
+template <int D, int G>
+__device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8], float (*red)[G][D + 4],
+                                const Coh& part, uint32_t tag) {
+  constexpr int LPR = D / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = tid % LPR;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    uint32_t mb = __float_as_uint(m[j]);
+    if (LPR == 8) mb = OpFmax{}(mb, dpp_row_ror8(mb));
+    const float mw = __uint_as_float(across_rows(mb, OpFmax{}));
+    const float f = scale_from(m[j], mw);
+    uint32_t lb = __float_as_uint(l[j] * f);
+    if (LPR == 8) lb = OpFadd{}(lb, dpp_row_ror8(lb));
+    const float lw = __uint_as_float(across_rows(lb, OpFadd{}));
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t ab = __float_as_uint(acc[j][e] * f);
+      if (LPR == 8) ab = OpFadd{}(ab, dpp_row_ror8(ab));
+      a[e] = __uint_as_float(across_rows(ab, OpFadd{}));
+    }
+    if (lane < LPR) {
+      float* rw = red[wave][j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rw[4 + c * 8 + e] = a[e];
+      if (c == 0) {
+        rw[0] = mw;
+        rw[1] = lw;
+      }
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < G * D / 2; o += NT) {
+    const int j = o / (D / 2), d2 = o % (D / 2);
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, red[v][j][0]);
+    float a0 = 0.f, a1 = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float* rw = red[v][j];
+      const float f = scale_from(rw[0], Mx);
+      a0 = fmaf(rw[4 + 2 * d2], f, a0);
+      a1 = fmaf(rw[4 + 2 * d2 + 1], f, a1);
+      Ls = fmaf(rw[1], f, Ls);
+    }
+    const int h = j * (D + 2);
+    part.put_u64(h + 2 + 2 * d2, tagged(a0, tag));
+    part.put_u64(h + 3 + 2 * d2, tagged(a1, tag));
+    if (d2 == 0) {
+      part.put_u64(h, tagged(Mx, tag));
+      part.put_u64(h + 1, tagged(Ls, tag));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Control workgroup of chunk `chunk` of pair bg.
+// ---------------------------------------------------------------------------
 template <typename KV, int D, int G>
-__device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk,
-                            FusedLds<D, G>& L) {
-  constexpr int LPR = D / 8, RS = NCTL / LPR, PST = kPartStride(D), RPL = kChunk / RS;
-  constexpr int KT = D / 32, NW = NT / 64;
+__device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
+                          CtlLds<D, G>& L) {
+  constexpr int LPR = D / 8, RS = NT / LPR;
+  constexpr int KT = D / 32, CPR = D / 8, RPI = 64 / CPR, NMU = CPR;  // NMU: 64 rows per wave / RPI
   constexpr bool MF = std::is_same<KV, uint16_t>::value;
-  constexpr int RW = sizeof(KV) / 2;                     // uint4 words per 8 elements
-  constexpr int NBUF = (MF ? 4 * KT : 0) > RPL * RW ? 4 * KT : RPL * RW;
   const int b = bg / s.Hkv, g = bg % s.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform values live in scalar registers, so branches on them do not
-  // serialise the two halves of the workgroup
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool ctl = wave < NCTL / 64;
-  const int ct = ctl ? tid : tid - NCTL;  // thread index within its half
-  const int cw = ctl ? wave : wave - NCTL / 64;  // wave index within its half
-  const int rs = ct / LPR, c = ct % LPR;  // row slot, 8-channel slice
-  const int Lseq = clamp_len(io.seq_lens[b], s.max_blocks * s.bs);
+  const int rs = tid / LPR, c = tid % LPR;  // row slot, 8-channel slice
+  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
   const int M = (Lseq + s.bs - 1) / s.bs;
   const int kk = min(M, s.kmax);
   const bool ranked = kk > 0 && kk < M;
-  const bool need_mu = kk < M;               // logits of omitted blocks are needed
+  const bool need_mu = kk < M;  // logits of omitted blocks are needed
   const bool comp = need_mu && io.compensate;
   const int start = chunk * kChunk;
   const int nrows = max(0, min(M, start + kChunk) - start);
   const size_t row0 = (size_t)bg * s.max_blocks + start;  // logical summary row of the chunk
-  const KV* q = static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D;
   const KV* mk = static_cast<const KV*>(io.summ.mean_k) + row0 * D;
   const KV* mv = static_cast<const KV*>(io.summ.mean_v) + row0 * D;
   const int r = s.r, gs = D / r;
   const float* gv = io.summ.gvar + row0 * r;
   uint32_t* err = w.ctrl + 2;
 
-  // ---- loads: q; control: mean keys and variances; value: mean values ----
+  // ---- loads, all issued at once, oldest first: q, page-table entries, the
+  // matrix-operand rows of q, then the chunk's mean keys and variances.
+  // Buffer views end at the chunk's last block, so rows past it read 0. ----
+  const Buf qb(static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D, G * D * sizeof(KV));
+  const Buf btb(io.block_table + (size_t)b * s.max_blocks + start, kk > 0 ? nrows * 4 : 0);
+  const Buf mkb(mk, need_mu ? nrows * D * sizeof(KV) : 0);
+  const Buf gvb(gv, need_mu && ranked ? nrows * r * 4 : 0);
   Raw8<KV> qraw;
-  const bool qld = tid < G * D / 8;  // control threads only (G * D / 8 <= 128)
-  if (qld) raw_load(q + tid * 8, qraw);
-  uint4 buf[NBUF];  // control: mean-key MFMA operands; value: raw mean values
-  float4 gpre[4];
+  raw_load(qb, tid * 8, qraw);  // threads past G * D / 8 read 0
+  const int pge = (int)btb.u32(4 * tid);
   bf16x8_t qa[KT];
+  uint4 mu[NMU];
+  float4 gpre[4];
   const bool holder = (lane >> 4) * 4 < G;
-  if (ctl) {
-    if constexpr (MF) {
-      if (need_mu) {
-        const int head = lane & 15, kq = lane >> 4;
+  if constexpr (MF) {
+    const int head = lane & 15, kq = lane >> 4;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          uint4 v = make_uint4(0u, 0u, 0u, 0u);
-          if (head < G) v = *reinterpret_cast<const uint4*>(q + (size_t)head * D + 32 * kt + 8 * kq);
-          qa[kt] = __builtin_bit_cast(bf16x8_t, v);
-        }
+    for (int kt = 0; kt < KT; ++kt)
+      qa[kt] = __builtin_bit_cast(bf16x8_t, qb.u128(2 * (head * D + 32 * kt + 8 * kq)));  // 0 past G
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ri = (cw + 4 * u) * 16 + (lane & 15);
-          const bool ok = ri < nrows;
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-            buf[u * KT + kt] = ok ? *reinterpret_cast<const uint4*>(mk + (size_t)ri * D + 32 * kt + 8 * kq)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-          gpre[u] = (ok && holder && r == 4 && ranked) ? *reinterpret_cast<const float4*>(gv + (size_t)ri * 4)
-                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
+    for (int u = 0; u < NMU; ++u) {
+      const int row = 64 * wave + RPI * u + lane / CPR;
+      mu[u] = mkb.u128(2 * (row * D + (lane % CPR) * 8));
     }
-  } else if (comp) {
 #pragma unroll
-    for (int jj = 0; jj < RPL; ++jj) {
-      const int ri = rs + jj * RS;
-      Raw8<KV> x;
-      if (ri < nrows) raw_load(mv + (size_t)ri * D + c * 8, x);
-      else raw_zero(x);
-      if constexpr (MF) {
-        buf[jj] = x.a;
-      } else {
-        buf[2 * jj] = x.a;
-        buf[2 * jj + 1] = x.b;
-      }
-    }
+    for (int u = 0; u < 4; ++u) gpre[u] = gvb.f128(16 * (64 * wave + 16 * u + (lane & 15)));
   }
-  if (qld) {
+  // q rows to LDS; partial |q|^2 of each thread's 8 channels
+  {
     float x[8];
     raw_float(qraw, x);
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq = fmaf(x[e], x[e], sq);
+    // every thread stores (zeros past G * D / 8), so the load is not sunk
+    // below the mean-key loads into a branch
 #pragma unroll
     for (int e = 0; e < 8; ++e) L.qf[tid * 8 + e] = x[e];
+    L.qsq[tid] = sq;
   }
+  L.pgt[tid] = tid < nrows && pge >= 0 && pge < s.P ? pge : -1;
   __syncthreads();
+  // |q_h restricted to channel group t|^2, from the 8-channel partials when
+  // a group spans whole partials
   for (int item = tid; item < G * r; item += NT) {
     const int j = item / r, tg = item % r;
-    const float* qh = L.qf + j * D + tg * gs;
     float a = 0.f;
-    for (int cc = 0; cc < gs; ++cc) a = fmaf(qh[cc], qh[cc], a);
+    if (gs >= 8) {
+      const float* part = L.qsq + (j * D + tg * gs) / 8;
+      for (int cc = 0; cc < gs / 8; ++cc) a += part[cc];
+    } else {
+      const float* qh = L.qf + j * D + tg * gs;
+      for (int cc = 0; cc < gs; ++cc) a = fmaf(qh[cc], qh[cc], a);
+    }
     L.qn[item] = a;
   }
   __syncthreads();
 
-  // ---- block-mean logits and variance estimates (control waves) ----
-  if (ctl && need_mu) {
+  // ---- block-mean logits and variance estimates ----
+  if (need_mu) {
     if constexpr (MF) {
-      // D[head][row] = sum_k Q[head][k] mean_k[row][k]; lane l holds Q[l%16][8(l/16)..+7]
-      // of each 32-wide k-slice (zero rows past G), mean_k of row l%16 at the same
-      // k, and receives D[4(l/16)+i][l%16].
+      // Each wave turns its 64 rows, 16 at a time, into matrix operands through
+      // its own LDS tile (16-byte pieces swizzled by row, conflict-free both
+      // ways).  D[head][row] = sum_k Q[head][k] mean_k[row][k]; lane l holds
+      // Q[l%16][8(l/16)..+7] of each 32-wide k-slice (zero rows past G), mean_k
+      // of row l%16 at the same k, and receives D[4(l/16)+i][l%16].
+      uint4* st = L.u.stage[wave];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int g4 = 0; g4 < 4; ++g4) {
+#pragma unroll
+        for (int v = 0; v < 16 / RPI; ++v) {
+          const int rr = RPI * v + lane / CPR, ch = lane % CPR;
+          st[rr * CPR + (ch ^ (rr & (CPR - 1)))] = mu[g4 * (16 / RPI) + v];
+        }
+        __builtin_amdgcn_wave_barrier();
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kt], __builtin_bit_cast(bf16x8_t, buf[u * KT + kt]),
-                                                         acc, 0, 0, 0);
-        const int ri = (cw + 4 * u) * 16 + (lane & 15);
+        for (int kt = 0; kt < KT; ++kt) {
+          const int rr = lane & 15, ch = 4 * kt + (lane >> 4);
+          const uint4 bv = st[rr * CPR + (ch ^ (rr & (CPR - 1)))];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kt], __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int ri = 64 * wave + 16 * g4 + (lane & 15);
         if (ri < nrows && holder) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -221,10 +324,10 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
               float sig = 0.f;
               if (ranked) {
                 if (r == 4) {
-                  sig = fmaf(L.qn[j * 4 + 0], gpre[u].x, sig);
-                  sig = fmaf(L.qn[j * 4 + 1], gpre[u].y, sig);
-                  sig = fmaf(L.qn[j * 4 + 2], gpre[u].z, sig);
-                  sig = fmaf(L.qn[j * 4 + 3], gpre[u].w, sig);
+                  sig = fmaf(L.qn[j * 4 + 0], gpre[g4].x, sig);
+                  sig = fmaf(L.qn[j * 4 + 1], gpre[g4].y, sig);
+                  sig = fmaf(L.qn[j * 4 + 2], gpre[g4].z, sig);
+                  sig = fmaf(L.qn[j * 4 + 3], gpre[g4].w, sig);
                 } else {
                   for (int e = 0; e < r; ++e) sig = fmaf(L.qn[j * r + e], gv[(size_t)ri * r + e], sig);
                 }
@@ -272,10 +375,11 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
   // ---- per head: chunk max, Z_hat part, compensation weights, log-scores ----
   if (need_mu) {
     const Coh hdr(w.fhdr + (size_t)bg * s.n_chunks * G, (size_t)s.n_chunks * G * 8);
+    const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8);
     for (int j = wave; j < G; j += NW) {
       float mx = -INFINITY;
       for (int ri = lane; ri < nrows; ri += 64) mx = fmaxf(mx, L.sb[j][ri]);
-      mx = wave_max(mx);
+      mx = wave_max_dpp(mx);
       float z = 0.f;
       for (int ri = lane; ri < nrows; ri += 64) {
         const int n = min(s.bs, Lseq - (start + ri) * s.bs);
@@ -285,25 +389,24 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
         z = fmaf(wt, 1.f + half, z);
         L.wt[j][ri] = wt;
         L.lam[j][ri] = io.score_mode == kScoreMass ? sb + logf(massf) : sb + logf(massf * half);
+        if (comp) wts.put_u64(j * kWStride + ri, tagged(wt, tag));
       }
-      z = wave_sum(z);
+      z = wave_sum_dpp(z);
       if (lane == 0) {
         L.mx[j] = mx;
-        if (ranked)
-          hdr.put_u64(chunk * G + j, ((uint64_t)__float_as_uint(z) << 32) | __float_as_uint(mx));
+        if (ranked) hdr.put_u64(chunk * G + j, ((uint64_t)__float_as_uint(z) << 32) | __float_as_uint(mx));
+        if (comp) wts.put_u64(j * kWStride + kChunk, tagged(mx, tag));
       }
     }
   }
   __syncthreads();
 
-  // ---- selection ----
-  const int lo = chunk * s.share, hi = min(kk, lo + s.share);
-  const int nb = max(0, hi - lo);
-  int32_t* sel_out = (chunk == 0 && io.selected) ? io.selected + (size_t)bg * s.kmax : nullptr;
+  // ---- selection: which blocks of this chunk are attended exactly ----
+  int n_own = 0;
   if (ranked) {
     // log Z_hat per head from every chunk header of the pair
     const int nh = s.n_chunks * G;
-    if (ctl) {
+    {
       const Coh hdr(w.fhdr + (size_t)bg * nh, (size_t)nh * 8);
       read_published(hdr, nh, nh, 0, L.u.keys, err);
     }
@@ -311,13 +414,13 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
     for (int j = wave; j < G; j += NW) {
       float mz = -INFINITY;
       for (int ch = lane; ch < s.n_chunks; ch += 64) mz = fmaxf(mz, __uint_as_float((uint32_t)L.u.keys[ch * G + j]));
-      mz = wave_max(mz);
+      mz = wave_max_dpp(mz);
       float zs = 0.f;
       for (int ch = lane; ch < s.n_chunks; ch += 64) {
         const uint64_t h = L.u.keys[ch * G + j];
         zs += __uint_as_float((uint32_t)(h >> 32)) * scale_from(__uint_as_float((uint32_t)h), mz);
       }
-      zs = wave_sum(zs);
+      zs = wave_sum_dpp(zs);
       if (lane == 0) L.lnz[j] = zs > 0.f ? mz + logf(zs) : -INFINITY;
     }
     __syncthreads();
@@ -348,7 +451,7 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
     __syncthreads();
     // the pair's top-k from every chunk's candidates
     const int n2 = s.n_chunks * kk;
-    if (ctl) read_published(cand, n2, kk, s.kmax, L.u.keys, err);
+    read_published(cand, n2, kk, s.kmax, L.u.keys, err);
     const int words = (M + 31) / 32;
     for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
     __syncthreads();
@@ -359,35 +462,135 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
       if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
     }
     __syncthreads();
-    emit_selection<NT>(M, L.bitmap, L.wsum, sel_out, kk, L.blk, lo, hi);
-  } else {
-    // every block selected (kk == M), or none (kk == 0)
-    for (int e = tid; e < nb; e += NT) L.blk[e] = lo + e;
-    if (sel_out)
-      for (int i = tid; i < kk; i += NT) sel_out[i] = i;
+    // this chunk's selected blocks, ascending (kChunk / 32 bitmap words)
+    if (wave == 0) {
+      const int wd = start / 32 + lane;
+      const uint32_t bits = (lane < kChunk / 32 && wd < words) ? L.bitmap[wd] : 0u;
+      const uint32_t cnt = __popc(bits);
+      const uint32_t inc = wave_scan_incl(cnt);
+      uint32_t pos = inc - cnt;
+      for (uint32_t x = bits; x; x &= x - 1) L.own[pos++] = 32 * lane + __ffs(x) - 1;
+      if (lane == 63) L.count = inc;
+    }
+    __syncthreads();
+    n_own = (int)L.count;
+  } else if (kk == M) {
+    // every block selected
+    n_own = nrows;
+    L.own[tid] = tid;
     __syncthreads();
   }
-  if (chunk == 0) {
-    if (tid == 0 && io.num_selected) io.num_selected[bg] = kk;
-    if (sel_out)
-      for (int e = kk + tid; e < s.kmax; e += NT) sel_out[e] = -1;
-  }
 
-  // ---- pages of this workgroup's share of the selected blocks ----
-  if (ctl) {
-    for (int e = ct; e < nb; e += NCTL) {
-      const int i = L.blk[e];
-      int p = -1, n = 0;
-      if (i >= 0 && i < M) {
-        p = io.block_table[(size_t)b * s.max_blocks + i];
-        if (p < 0 || p >= s.P) p = -1;
-        else n = min(s.bs, Lseq - i * s.bs);
+  // ---- exact attention over the chunk's selected blocks ----
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  }
+  {
+    // one batch covers UG tokens per row slot (8 blocks per workgroup); all
+    // its loads, and those of the take-back rows, are issued together
+    constexpr int UG = 8;
+    const KV* kc = static_cast<const KV*>(io.k_cache);
+    const KV* vc = static_cast<const KV*>(io.v_cache);
+    float qv[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[j][e] = L.qf[j * D + c * 8 + e];
+    const int ntok = n_own * kBlockSize;
+    // The value workgroup sums the compensation terms of every block of the
+    // chunk; the terms of the selected ones are taken back here, as the
+    // starting state (frame: the chunk max) of the exact softmax.
+    const bool take_back = comp && n_own > 0;
+    if (take_back) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) m[j] = L.mx[j];
+    }
+    for (int t0 = 0; t0 < max(ntok, take_back ? n_own : 0); t0 += RS * UG) {
+      Raw8<KV> kr[UG], vr[UG];
+      bool ok[UG];
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const int R = t0 + u * RS + rs;
+        const int ri = R < ntok ? L.own[R / kBlockSize] : 0, tok = R % kBlockSize;
+        const int pg = L.pgt[ri];
+        ok[u] = R < ntok && pg >= 0 && tok < Lseq - (start + ri) * s.bs;
+        if (ok[u]) {
+          const size_t off = (((size_t)pg * s.Hkv + g) * s.bs + tok) * D + c * 8;
+          raw_load(kc + off, kr[u]);
+          raw_load(vc + off, vr[u]);
+        }
       }
-      L.pg[e] = p;
-      L.nn[e] = n;
+      if (take_back) {
+        // the selected rows' mean values: row slot rs takes rows e = t0/16 + rs, ...
+        // The weights are in the chunk-max frame; earlier batches may have
+        // raised the row's running max above it.
+        for (int e = t0 / kBlockSize + rs; e < min(n_own, (t0 + RS * UG) / kBlockSize); e += RS) {
+          const int ri = L.own[e];
+          float nv[8];
+          load8(mv + (size_t)ri * D + c * 8, nv);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const float wt = L.wt[j][ri] * (t0 == 0 ? 1.f : expf(L.mx[j] - m[j]));
+            l[j] -= wt;
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) acc[j][e2] = fmaf(-wt, nv[e2], acc[j][e2]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        if (ok[u]) {  // uniform across the row's lanes
+          float k8[8], v8[8], dot[G];
+          raw_float(kr[u], k8);
+          raw_float(vr[u], v8);
+          dot8<G>(qv, k8, dot);
+#pragma unroll
+          for (int j = 0; j < G; ++j) online_add<G>(m, l, acc, j, group_sum<LPR>(dot[j]) * s.tau, 1.f, v8);
+        }
+      }
     }
   }
-  __syncthreads();
+  const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + chunk) * G * (D + 2), (size_t)G * (D + 2) * 8);
+  publish_partial<D, G>(m, l, acc, L.u.red, part, tag);
+
+  // ---- the selection outputs ----
+  if (chunk == 0) {
+    int32_t* out = io.selected ? io.selected + (size_t)bg * s.kmax : nullptr;
+    if (tid == 0 && io.num_selected) io.num_selected[bg] = kk;
+    if (out) {
+      for (int e = kk + tid; e < s.kmax; e += NT) out[e] = -1;
+      if (ranked) emit_selection<NT>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
+      else
+        for (int i = tid; i < kk; i += NT) out[i] = i;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Value workgroup of chunk `chunk` of pair bg: the compensation terms of every
+// block of the chunk, n e^{s_bar} mean_v, with the control workgroup's weights.
+// ---------------------------------------------------------------------------
+template <typename KV, int D, int G>
+__device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
+                          ValLds<D, G>& L) {
+  constexpr int LPR = D / 8, RS = NT / LPR, RPL = kChunk / RS;
+  const int b = bg / s.Hkv;
+  const int tid = threadIdx.x;
+  const int rs = tid / LPR, c = tid % LPR;
+  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
+  const int M = (Lseq + s.bs - 1) / s.bs;
+  const int kk = min(M, s.kmax);
+  const bool comp = kk < M && io.compensate;
+  const int start = chunk * kChunk;
+  const int nrows = max(0, min(M, start + kChunk) - start);
+  const Buf mvb(static_cast<const KV*>(io.summ.mean_v) + ((size_t)bg * s.max_blocks + start) * D,
+                nrows * D * sizeof(KV));
+  uint32_t* err = w.ctrl + 2;
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -397,254 +600,161 @@ __device__ bool fused_chunk(const Shape& s, const StepIO& io, const Work& w, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
-  if (ctl) {
-    // ---- exact attention over the share's tokens (control waves) ----
-    constexpr int UG = 2;  // token rows per lane per batch
-    const KV* kc = static_cast<const KV*>(io.k_cache);
-    const KV* vc = static_cast<const KV*>(io.v_cache);
-    float qv[G][8];
+  if (comp) {
+    const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8);
+    uint32_t spins = 0;
+    // the chunk maxima come last from the control workgroup: once they are
+    // here, its mean keys have arrived and the mean values may stream
+    if (tid < G) L.mx[tid] = read_tagged(wts, tid * kWStride + kChunk, wts.u64(tid * kWStride + kChunk), tag, spins, err);
+    __syncthreads();
+    Raw8<KV> nu[RPL];
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+    for (int jj = 0; jj < RPL; ++jj) raw_load(mvb, (rs + jj * RS) * D + c * 8, nu[jj]);  // 0 past the chunk
+    // this thread's weights: row tid of every head, all requested together
+    uint64_t wv[G];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[j][e] = L.qf[j * D + c * 8 + e];
-    const int ntok = nb * kBlockSize;
-    const int nbatch = (ntok + RS * UG - 1) / (RS * UG);
-    Raw8<KV> kr[UG], vr[UG];
-    bool ok[UG];
-    // software pipeline: the next batch is in flight while this one is used
-#define CKV_ISSUE(BI)                                                                   \
-  _Pragma("unroll") for (int u = 0; u < UG; ++u) {                                      \
-    const int R = ((BI) * UG + u) * RS + rs;                                            \
-    const int bl = R / kBlockSize, tok = R % kBlockSize;                                \
-    ok[u] = R < ntok && L.pg[bl] >= 0 && tok < L.nn[bl];                                \
-    if (ok[u]) {                                                                        \
-      const size_t off = (((size_t)L.pg[bl] * s.Hkv + g) * s.bs + tok) * D + c * 8;     \
-      raw_load(kc + off, kr[u]);                                                        \
-      raw_load(vc + off, vr[u]);                                                        \
-    }                                                                                   \
-  }
-    if (nbatch > 0) { CKV_ISSUE(0) }
-    for (int bi = 0; bi < nbatch; ++bi) {
-      float k8[UG][8], v8[UG][8];
-      bool okc[UG];
+    for (int j = 0; j < G; ++j) wv[j] = tid < nrows ? wts.u64(j * kWStride + tid) : 0u;
+    if (tid < nrows) {
 #pragma unroll
-      for (int u = 0; u < UG; ++u) {
-        okc[u] = ok[u];
-        if (ok[u]) {
-          raw_float(kr[u], k8[u]);
-          raw_float(vr[u], v8[u]);
-        }
-      }
-      if (bi + 1 < nbatch) { CKV_ISSUE(bi + 1) }
-#pragma unroll
-      for (int u = 0; u < UG; ++u) {
-        if (okc[u]) {  // uniform across the row's lanes
-          float dot[G];
-          dot8<G>(qv, k8[u], dot);
-#pragma unroll
-          for (int j = 0; j < G; ++j) online_add<G>(m, l, acc, j, group_sum<LPR>(dot[j]) * s.tau, 1.f, v8[u]);
-        }
-      }
+      for (int j = 0; j < G; ++j) L.w[j][tid] = read_tagged(wts, j * kWStride + tid, wv[j], tag, spins, err);
     }
-#undef CKV_ISSUE
-  } else if (comp) {
-    // ---- compensation of the chunk's omitted blocks (value waves) ----
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < G; ++j) m[j] = L.mx[j];
 #pragma unroll
     for (int jj = 0; jj < RPL; ++jj) {
       const int ri = rs + jj * RS;
       if (ri < nrows) {
-        const int blk = start + ri;
-        const bool taken = ranked && ((L.bitmap[blk >> 5] >> (blk & 31)) & 1u);
-        if (!taken) {
-          Raw8<KV> raw;
-          if constexpr (MF) {
-            raw.a = buf[jj];
-          } else {
-            raw.a = buf[2 * jj];
-            raw.b = buf[2 * jj + 1];
-          }
-          float x[8];
-          raw_float(raw, x);
+        float x[8];
+        raw_float(nu[jj], x);
 #pragma unroll
-          for (int j = 0; j < G; ++j) {
-            const float wt = L.wt[j][ri];
-            l[j] += wt;
+        for (int j = 0; j < G; ++j) {
+          const float wt = L.w[j][ri];
+          l[j] += wt;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(wt, x[e], acc[j][e]);
-          }
+          for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(wt, x[e], acc[j][e]);
         }
       }
     }
   }
-
-  // ---- one partial per head: combine row slots, then waves ----
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float mw = m[j];
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
-    const float f = scale_from(m[j], mw);
-    float lj = l[j] * f;
-    float a[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = acc[j][e] * f;
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
-      lj += __shfl_xor(lj, o, 64);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] += __shfl_xor(a[e], o, 64);
-    }
-    if (lane < LPR) {
-      float* rw = L.u.red[wave][j];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rw[4 + c * 8 + e] = a[e];
-      if (c == 0) {
-        rw[0] = mw;
-        rw[1] = lj;
-      }
-    }
-  }
-  __syncthreads();
-  {
-    const Coh part(w.cpart + ((size_t)bg * s.n_chunks + chunk) * G * PST, (size_t)G * PST * 4);
-    for (int o = tid; o < G * D / 4; o += NT) {
-      const int j = o / (D / 4), d4 = o % (D / 4);
-      float Mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, L.u.red[v][j][0]);
-      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-      float Ls = 0.f;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) {
-        const float* rw = L.u.red[v][j];
-        const float f = scale_from(rw[0], Mx);
-        A.x = fmaf(rw[4 + 4 * d4 + 0], f, A.x);
-        A.y = fmaf(rw[4 + 4 * d4 + 1], f, A.y);
-        A.z = fmaf(rw[4 + 4 * d4 + 2], f, A.z);
-        A.w = fmaf(rw[4 + 4 * d4 + 3], f, A.w);
-        Ls = fmaf(rw[1], f, Ls);
-      }
-      part.put4(j * PST + 4 + 4 * d4, A);
-      if (d4 == 0) {
-        part.put(j * PST, Mx);
-        part.put(j * PST + 1, Ls);
-      }
-    }
-  }
-  return arrive(w.ctrl + kCtrlHeader + 4 * bg + 2, &L.slot) == (uint32_t)(s.n_chunks - 1);
+  const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
+                 (size_t)G * (D + 2) * 8);
+  publish_partial<D, G>(m, l, acc, L.red, part, tag);
 }
 
-// Merge the pair's chunk partials into out and lse; clear the pair's
-// published words and counter.
+// ---------------------------------------------------------------------------
+// Workgroup `slot` (of the pair's 2 * n_chunks) merges its slice of the
+// pair's output from all the pair's partials, waiting for each to carry this
+// call's tag.  The last workgroup to finish resets the pair for the next call.
+// ---------------------------------------------------------------------------
 template <int D, int G>
-__device__ void fused_merge(const Shape& s, const StepIO& io, const Work& w, int bg, FusedLds<D, G>& L) {
-  constexpr int PST = kPartStride(D), NV = G * D / 4, TPO = NT / NV, NW = NT / 64;
-  constexpr int PB = 8;   // partials per thread per round trip
-  static_assert(NV <= NT && TPO <= 64, "one float4 output per group of lanes");
+__device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int bg, int slot, uint32_t epoch,
+                            MergeLds<D, G>& L, uint32_t* sh) {
+  constexpr int NV = G * D / 4;
   const int b = bg / s.Hkv, g = bg % s.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = s.n_chunks;
-  const Coh part(w.cpart + (size_t)bg * nch * G * PST, (size_t)nch * G * PST * 4);
-  const int o = tid / TPO, sub = tid % TPO;
-  const int j = o / (D / 4), d4 = o % (D / 4);
-  // (max, sum) of every partial and the first batch of accumulators, together
-  float mi = 0.f, li = 0.f;
-  if (tid < nch * G) {
-    mi = part.f32(tid * PST);
-    li = part.f32(tid * PST + 1);
-  }
-  float4 av[PB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t tag = epoch + 1u;
+  uint32_t* err = w.ctrl + 2;
+  const int np = 2 * s.n_chunks;
+  const int per = (NV + np - 1) / np;  // float4 outputs of this workgroup
+  const int step = max(1, NT / np);    // outputs merged per pass
+  const int o0 = slot * per, o1 = min(NV, o0 + per);
+  const Coh part(w.fpart + (size_t)bg * np * G * (D + 2), (size_t)np * G * (D + 2) * 8);
+  uint32_t spins = 0;
+  for (int base = o0; base < o1; base += step) {
+    // the (output, partial) items of this pass: six words each, read together
+    const int nout = min(o1 - base, step);
+    for (int it = tid; it < nout * np; it += NT) {
+      const int o = base + it / np, p = it % np;
+      const int j = o / (D / 4), d4 = o % (D / 4);
+      const int h = (p * G + j) * (D + 2);
+      uint64_t v[6];
+      v[0] = part.u64(h);
+      v[1] = part.u64(h + 1);
 #pragma unroll
-  for (int u = 0; u < PB; ++u) {
-    const int p = sub + u * TPO;
-    av[u] = p < nch ? part.f32x4((p * G + j) * PST + 4 + 4 * d4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (tid < nch * G) {
-    L.hdr[2 * tid] = mi;
-    L.hdr[2 * tid + 1] = li;
-  }
-  __syncthreads();
-  for (int jj = wave; jj < G; jj += NW) {
-    float Mx = -INFINITY;
-    for (int p = lane; p < nch; p += 64) Mx = fmaxf(Mx, L.hdr[2 * (p * G + jj)]);
-    Mx = wave_max(Mx);
-    float Ls = 0.f;
-    for (int p = lane; p < nch; p += 64) {
-      const float f = scale_from(L.hdr[2 * (p * G + jj)], Mx);
-      L.u.fac[p * G + jj] = f;
-      Ls = fmaf(L.hdr[2 * (p * G + jj) + 1], f, Ls);
+      for (int e = 0; e < 4; ++e) v[2 + e] = part.u64(h + 2 + 4 * d4 + e);
+      L.pm[it] = read_tagged(part, h, v[0], tag, spins, err);
+      L.pl[it] = read_tagged(part, h + 1, v[1], tag, spins, err);
+      float4 a;
+      a.x = read_tagged(part, h + 2 + 4 * d4, v[2], tag, spins, err);
+      a.y = read_tagged(part, h + 3 + 4 * d4, v[3], tag, spins, err);
+      a.z = read_tagged(part, h + 4 + 4 * d4, v[4], tag, spins, err);
+      a.w = read_tagged(part, h + 5 + 4 * d4, v[5], tag, spins, err);
+      L.pa[it] = a;
     }
-    Ls = wave_sum(Ls);
-    if (lane == 0) {
-      L.mtot[jj] = Mx;
-      L.ltot[jj] = Ls;
-    }
-  }
-  __syncthreads();
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = 0; base < nch; base += PB * TPO) {
-    if (base > 0) {
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int p = base + sub + u * TPO;
-        av[u] = p < nch ? part.f32x4((p * G + j) * PST + 4 + 4 * d4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    for (int oo = wave; oo < nout; oo += NW) {
+      const int o = base + oo;
+      const int j = o / (D / 4), d4 = o % (D / 4);
+      float Mx = -INFINITY;
+      for (int p = lane; p < np; p += 64) Mx = fmaxf(Mx, L.pm[oo * np + p]);
+      Mx = wave_max_dpp(Mx);
+      float Ls = 0.f;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = lane; p < np; p += 64) {
+        const int it = oo * np + p;
+        const float f = scale_from(L.pm[it], Mx);
+        Ls = fmaf(L.pl[it], f, Ls);
+        A.x = fmaf(L.pa[it].x, f, A.x);
+        A.y = fmaf(L.pa[it].y, f, A.y);
+        A.z = fmaf(L.pa[it].z, f, A.z);
+        A.w = fmaf(L.pa[it].w, f, A.w);
+      }
+      Ls = wave_sum_dpp(Ls);
+      A.x = wave_sum_dpp(A.x);
+      A.y = wave_sum_dpp(A.y);
+      A.z = wave_sum_dpp(A.z);
+      A.w = wave_sum_dpp(A.w);
+      if (lane == 0) {
+        const int h = g * G + j;
+        float* op = io.out + ((size_t)b * s.Hq + h) * D + 4 * d4;
+        op[0] = Ls > 0.f ? A.x / Ls : 0.f;
+        op[1] = Ls > 0.f ? A.y / Ls : 0.f;
+        op[2] = Ls > 0.f ? A.z / Ls : 0.f;
+        op[3] = Ls > 0.f ? A.w / Ls : 0.f;
+        if (d4 == 0 && io.lse) io.lse[(size_t)b * s.Hq + h] = Ls > 0.f ? Mx + logf(Ls) : -INFINITY;
       }
     }
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int p = base + sub + u * TPO;
-      if (p < nch) {
-        const float f = L.u.fac[p * G + j];
-        a.x = fmaf(av[u].x, f, a.x);
-        a.y = fmaf(av[u].y, f, a.y);
-        a.z = fmaf(av[u].z, f, a.z);
-        a.w = fmaf(av[u].w, f, a.w);
-      }
-    }
+    __syncthreads();
   }
-#pragma unroll
-  for (int x = 1; x < TPO; x <<= 1) {
-    a.x += __shfl_xor(a.x, x, 64);
-    a.y += __shfl_xor(a.y, x, 64);
-    a.z += __shfl_xor(a.z, x, 64);
-    a.w += __shfl_xor(a.w, x, 64);
-  }
-  if (sub == 0) {
-    const float den = L.ltot[j];
-    const int h = g * G + j;
-    float* op = io.out + ((size_t)b * s.Hq + h) * D + 4 * d4;
-    op[0] = den > 0.f ? a.x / den : 0.f;
-    op[1] = den > 0.f ? a.y / den : 0.f;
-    op[2] = den > 0.f ? a.z / den : 0.f;
-    op[3] = den > 0.f ? a.w / den : 0.f;
-    if (d4 == 0 && io.lse) io.lse[(size_t)b * s.Hq + h] = den > 0.f ? L.mtot[j] + logf(den) : -INFINITY;
-  }
-  // leave the pair's published words cleared for the next call
-  const int Lseq = clamp_len(io.seq_lens[b], s.max_blocks * s.bs);
+  // the last workgroup of the pair to finish resets it for the next call
+  if (arrive(ctr_done(w, bg), sh) != (uint32_t)(np - 1)) return;
+  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
   const int M = (Lseq + s.bs - 1) / s.bs;
   const int kk = min(M, s.kmax);
   if (kk > 0 && kk < M) {
+    const int nch = s.n_chunks;
     const Coh hdr(w.fhdr + (size_t)bg * nch * G, (size_t)nch * G * 8);
     for (int e = tid; e < nch * G; e += NT) hdr.put_u64(e, 0u);
     const Coh cand(w.fcand + (size_t)bg * nch * s.kmax, (size_t)nch * s.kmax * 8);
     for (int e = tid; e < nch * kk; e += NT) cand.put_u64((e / kk) * s.kmax + e % kk, 0u);
   }
-  if (tid == 0) st_c(w.ctrl + kCtrlHeader + 4 * bg + 2, 0u);
+  if (tid == 0) {
+    st_c(ctr_done(w, bg), 0u);
+    st_c(ctr_epoch(w, bg), epoch + 1u);
+  }
 }
 
 template <typename KV, int D, int G>
-__global__ __launch_bounds__(NT) void fused_step_kernel(Shape s, StepIO io, Work w) {
+__global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
   __shared__ FusedLds<D, G> lds;
-  const int chunk = (int)blockIdx.x % s.n_chunks;
-  for (int bg = (int)blockIdx.x / s.n_chunks; bg < s.B * s.Hkv; bg += s.bg_round) {
-    if (fused_chunk<KV, D, G>(s, io, w, bg, chunk, lds)) fused_merge<D, G>(s, io, w, bg, lds);
+  __shared__ uint32_t sh[4];
+  const int half = s.bg_round * s.n_chunks;
+  const bool ctl = (int)blockIdx.x < half;
+  const int t = ctl ? (int)blockIdx.x : (int)blockIdx.x - half;
+  const int chunk = t % s.n_chunks;
+  for (int bg = t / s.n_chunks; bg < s.B * s.Hkv; bg += s.bg_round) {
+    const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
+    if (ctl) ctl_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.c);
+    else val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
+    __syncthreads();
+    merge_slice<D, G>(s, io, w, bg, ctl ? chunk : s.n_chunks + chunk, epoch, lds.m, sh);
     __syncthreads();
   }
 }
 
-// Calls f(kernel) with the fused kernel instance for (dtype, D, G).
+// Calls f(kernel, index) with the fused kernel instance for (dtype, D, G).
 template <class F>
 auto with_fused(const Shape& s, F&& f) {
 #define CKV_G(KV, DD)                                          \
@@ -684,7 +794,7 @@ int fused_resident_workgroups(const Shape& s) {
 }
 
 hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t st) {
-  const dim3 grid(s.bg_round * s.n_chunks);
+  const dim3 grid(2 * s.bg_round * s.n_chunks);
   return with_fused(s, [&](auto fn, int) {
     hipLaunchKernelGGL(fn, grid, dim3(NT), 0, st, s, io, w);
     return hipGetLastError();

@@ -20,10 +20,10 @@ constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks
 constexpr int kCandLds = 2048;      // second-level candidates kept in LDS (else read from memory)
 constexpr int kShareMax = 256;      // selected blocks one fused workgroup attends to
 constexpr int kMaxChunks = (kMaxBlocks + kChunk - 1) / kChunk;
-constexpr int kFusedThreads = 512;  // fused step: 4 control waves + 4 value waves
 constexpr int kFusedCand = 4608;    // fused step: candidates of all chunks held in LDS
 constexpr int kPartStride(int d) { return d + 4; }  // [m, l, z, c, acc[d]]
 constexpr int kCtrlHeader = 64;     // uint32 words before the per-(sequence, KV head) counters
+constexpr int kCtrlPerPair = 8;     // control words per (sequence, KV head)
 
 enum ScoreMode { kScoreCompKV = 0, kScoreMass = 1 };
 
@@ -53,8 +53,9 @@ struct Shape {
 
 // Device pointers carved from the caller's workspace.
 struct Work {
-  uint32_t* ctrl;  // [kCtrlHeader + 4 * B * Hkv]: error flag at 2; per (b, g): scan-A
-                   //   arrivals, select arrivals, merge arrivals, (spare)
+  uint32_t* ctrl;  // [kCtrlHeader + kCtrlPerPair * B * Hkv]: error flag at 2; per (b, g):
+                   //   (spare), select arrivals, attend arrivals, fused epoch, fused
+                   //   arrivals, fused merges done, (spare x2)
   float* xs;       // [B][Hq][max_blocks]  exp(log score - chunk max of log score)
   float* cpart;    // [B][Hkv][n_chunks][G][D+4]  per chunk and head: max s_bar, sum w,
                    //   sum w (1 + var_hat/2), max log score, sum w mean_v; w = n e^{s_bar - max}
@@ -63,6 +64,10 @@ struct Work {
                    //   blocks' own compensation terms
   uint64_t* fhdr;  // [B][Hkv][n_chunks][G] fused: chunk header (max s_bar, Z_hat part), 0 = unset
   uint64_t* fcand; // [B][Hkv][n_chunks][kmax] fused: chunk candidates, 0 = unset
+  uint64_t* fw;    // [B][Hkv][n_chunks][G][kChunk + 1] fused: compensation weights and chunk
+                   //   max, epoch-tagged
+  uint64_t* fpart; // [B][Hkv][2 * n_chunks][G][D+2] fused: control and value partials
+                   //   (max, sum, acc[D]), epoch-tagged
 };
 
 struct Summ {

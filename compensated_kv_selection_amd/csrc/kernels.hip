@@ -138,7 +138,7 @@ struct SelLds {
   float hc[kMaxChunks * 8];
   float lnz[8];
   float f[kSlice / kChunk][8];
-  uint32_t sh[4];
+  uint32_t sh[64];
   uint32_t wsum[kThreads / 64];
   uint32_t count;
 };
@@ -464,7 +464,7 @@ __device__ void slice_role(const Shape& s, const StepIO& io, const Work& w, int 
     }
     for (int e = k1 + tid; e < kk; e += kThreads) cand.put_u64(slice * s.kmax + e, 0u);  // below every real key
   }
-  const uint32_t prev = arrive(w.ctrl + kCtrlHeader + 4 * bg + 1, slot);
+  const uint32_t prev = arrive(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 1, slot);
   if (prev != (uint32_t)(s.n_slices - 1)) return;
 
   // the last slice of this (sequence, KV head): global top-k and the selection
@@ -504,7 +504,7 @@ __device__ void slice_role(const Shape& s, const StepIO& io, const Work& w, int 
     __syncthreads();
     emit_selection<kThreads>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
   }
-  if (tid == 0) st_c(w.ctrl + kCtrlHeader + 4 * bg + 1, 0u);
+  if (tid == 0) st_c(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 1, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -677,7 +677,7 @@ __device__ int gather_role(const Shape& s, const StepIO& io, const Work& w, int 
   __syncthreads();
   float* gp = w.gpart + ((size_t)bg * s.n_splits + split) * G * SLOT;
   gather_core<KV, D, G>(s, io, b, g, blk, nb, !DENSE && io.compensate != 0, gp, SLOT, L);
-  const uint32_t prev = arrive(w.ctrl + kCtrlHeader + 4 * bg + 2, slot);
+  const uint32_t prev = arrive(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 2, slot);
   return prev == (uint32_t)(s.n_splits - 1) ? bg : -1;
 }
 
@@ -770,7 +770,7 @@ __device__ void merge_role(const Shape& s, const StepIO& io, const Work& w, int 
     io.out[oi] = den > 0.f ? (ae * L.head[j][0] + ao * L.head[j][1]) / den : 0.f;
     if (io.lse && d == 0) io.lse[(size_t)b * s.Hq + h] = den > 0.f ? L.head[j][4] + logf(den) : -INFINITY;
   }
-  if (tid == 0) st_c(w.ctrl + kCtrlHeader + 4 * bg + 2, 0u);
+  if (tid == 0) st_c(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 2, 0u);
 }
 
 // ---------------------------------------------------------------------------

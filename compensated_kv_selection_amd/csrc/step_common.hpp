@@ -78,6 +78,33 @@ struct Coh {
   }
 };
 
+// A read-only buffer view of `bytes` bytes at `base` for plain loads (byte
+// offsets).  Reads past the end return 0 without touching memory, so range
+// checks need no branches and every load of a batch is issued unconditionally.
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ Buf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                            (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu), kRsrcWord3)) {}
+  __device__ uint4 u128(uint32_t off) const {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __device__ float4 f128(uint32_t off) const {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
+  __device__ uint32_t u32(uint32_t off) const { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+};
+
+// A word that no workgroup writes during the launch, read through the scalar
+// cache (uniform address): the wait for it does not hold vector loads.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  typedef const __attribute__((address_space(4))) T* const_p;
+  return *(const_p)p;
+}
+
 // Wait until *p >= target (bounded; running out sets the error word).
 __device__ __forceinline__ void wait_at_least(uint32_t* p, uint32_t target, uint32_t* err) {
   if (threadIdx.x == 0) {
@@ -115,6 +142,12 @@ __device__ __forceinline__ void raw_load(const float* p, Raw8<float>& r) {
   r.a = q[0];
   r.b = q[1];
 }
+// Eight elements at element offset e of a buffer view.
+__device__ __forceinline__ void raw_load(const Buf& b, uint32_t e, Raw8<uint16_t>& r) { r.a = b.u128(2 * e); }
+__device__ __forceinline__ void raw_load(const Buf& b, uint32_t e, Raw8<float>& r) {
+  r.a = b.u128(4 * e);
+  r.b = b.u128(4 * e + 16);
+}
 __device__ __forceinline__ void raw_zero(Raw8<uint16_t>& r) { r.a = make_uint4(0u, 0u, 0u, 0u); }
 __device__ __forceinline__ void raw_zero(Raw8<float>& r) { r.a = r.b = make_uint4(0u, 0u, 0u, 0u); }
 __device__ __forceinline__ void raw_float(const Raw8<uint16_t>& r, float (&x)[8]) {
@@ -144,24 +177,117 @@ struct LdsKeys {
   __device__ uint64_t operator()(int i) const { return p[i]; }
 };
 
+// ---- wave-wide cross-lane operations (DPP and permlane swaps, no LDS) -----------
+__device__ __forceinline__ uint32_t dpp_quad_xor1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t dpp_quad_xor2(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);
+}
+// Combine 16-lane rows pairwise (rows 0-1, 2-3), then wave halves; each
+// result lane sees (low operand, high operand) in the same order.
+template <class Op>
+__device__ __forceinline__ uint32_t across_rows(uint32_t x, Op op) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op((uint32_t)p[0], (uint32_t)p[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op((uint32_t)h[0], (uint32_t)h[1]);
+}
+// Reduction over all 64 lanes; every lane receives the result.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+  x = op(x, dpp_quad_xor1(x));
+  x = op(x, dpp_quad_xor2(x));
+  x = op(x, dpp_row_ror4(x));
+  x = op(x, dpp_row_ror8(x));
+  return across_rows(x, op);
+}
+struct OpOr { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
+struct OpAnd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a & b; } };
+struct OpFmax {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+    const float x = __uint_as_float(a), y = __uint_as_float(b);
+    return __float_as_uint(x > y ? x : y);
+  }
+};
+struct OpFadd {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }
+};
+__device__ __forceinline__ float wave_max_dpp(float x) { return __uint_as_float(wave_reduce(__float_as_uint(x), OpFmax{})); }
+__device__ __forceinline__ float wave_sum_dpp(float x) { return __uint_as_float(wave_reduce(__float_as_uint(x), OpFadd{})); }
+
+// Inclusive prefix sum over the 64 lanes (rows of 16 by shifts, then row
+// totals broadcast to the following rows).
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return x;
+}
+
 // Radix select of the k-th largest of n 64-bit keys (distinct among the k
-// largest), 8 bits per pass from the top, by the NT threads of the
-// workgroup.  Returns T such that exactly k keys are >= T; 1 <= k <= n.
-// hist: 512 words of LDS (two histograms used alternately), sh: 4 words.
+// largest), by the NT threads of the workgroup.  Bits shared by every key
+// are skipped; the rest is resolved 8 bits per pass from the top.  Returns T
+// such that exactly k keys are >= T; 1 <= k <= n.
+// hist: 512 words of LDS (two histograms used alternately), sh: 64 words.
 template <int NT, class KeyAt>
 __device__ uint64_t radix_kth_largest(const KeyAt key_at, int n, int k, uint32_t* hist, uint32_t* sh) {
+  constexpr int NW = NT / 64;
+  static_assert(NW <= 12, "scratch words");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t prefix = 0, pmask = 0;
-  uint32_t krem = (uint32_t)k;
+  uint64_t kor = 0, kand = ~0ull;
+  for (int i = tid; i < n; i += NT) {
+    const uint64_t key = key_at(i);
+    kor |= key;
+    kand &= key;
+  }
+  const uint32_t ohi = wave_reduce((uint32_t)(kor >> 32), OpOr{}), olo = wave_reduce((uint32_t)kor, OpOr{});
+  const uint32_t ahi = wave_reduce((uint32_t)(kand >> 32), OpAnd{}), alo = wave_reduce((uint32_t)kand, OpAnd{});
+  if (lane == 0) {
+    sh[16 + 4 * wave] = ohi;
+    sh[17 + 4 * wave] = olo;
+    sh[18 + 4 * wave] = ahi;
+    sh[19 + 4 * wave] = alo;
+  }
   for (int e = tid; e < 512; e += NT) hist[e] = 0u;
   __syncthreads();
-  for (int shift = 56, pass = 0; shift >= 0; shift -= 8, ++pass) {
+  uint64_t all_or = 0, all_and = ~0ull;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    all_or |= ((uint64_t)sh[16 + 4 * v] << 32) | sh[17 + 4 * v];
+    all_and &= ((uint64_t)sh[18 + 4 * v] << 32) | sh[19 + 4 * v];
+  }
+  const uint64_t diff = all_or ^ all_and;
+  if (diff == 0) {  // every key equal
+    __syncthreads();
+    return all_and;
+  }
+  const int hb = 63 - __clzll((long long)diff);
+  const uint64_t below = hb == 63 ? ~0ull : ((1ull << (hb + 1)) - 1);
+  uint64_t prefix = all_and & ~below, pmask = ~below;
+  uint32_t krem = (uint32_t)k;
+  for (int top = hb, pass = 0; top >= 0; top -= 8, ++pass) {
+    const int lo = top - 7;  // lowest bit of this digit (may be below bit 0)
     uint32_t* h = hist + 256 * (pass & 1);
     uint32_t* h_next = hist + 256 * ((pass + 1) & 1);
     for (int e = tid; e < 256; e += NT) h_next[e] = 0u;
     for (int i = tid; i < n; i += NT) {
       const uint64_t key = key_at(i);
-      if ((key & pmask) == prefix) atomicAdd(&h[(uint32_t)(key >> shift) & 255u], 1u);
+      if ((key & pmask) == prefix) {
+        const uint32_t d = (uint32_t)((lo >= 0 ? key >> lo : key << -lo) & 255u);
+        atomicAdd(&h[d], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -169,13 +295,7 @@ __device__ uint64_t radix_kth_largest(const KeyAt key_at, int n, int k, uint32_t
 #pragma unroll
       for (int e = 0; e < 4; ++e) cs[e] = h[255 - 4 * lane - e];  // descending digits
       const uint32_t loc = cs[0] + cs[1] + cs[2] + cs[3];
-      uint32_t inc = loc;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += y;
-      }
-      uint32_t cum = inc - loc;  // keys with a larger digit
+      uint32_t cum = wave_scan_incl(loc) - loc;  // keys with a larger digit
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (cum < krem && cum + cs[e] >= krem) {
@@ -189,8 +309,8 @@ __device__ uint64_t radix_kth_largest(const KeyAt key_at, int n, int k, uint32_t
     __syncthreads();
     const uint32_t digit = sh[0], above = sh[1], cnt = sh[2];
     krem -= above;
-    prefix |= (uint64_t)digit << shift;
-    pmask |= (uint64_t)255u << shift;
+    prefix |= lo >= 0 ? (uint64_t)digit << lo : (uint64_t)digit >> -lo;
+    pmask |= lo >= 0 ? 255ull << lo : 255ull >> -lo;
     if (cnt == krem) break;  // every key with this prefix is taken
   }
   __syncthreads();  // sh and the histograms may be reused by the caller
@@ -210,12 +330,7 @@ __device__ void emit_selection(int M, const uint32_t* bitmap, uint32_t* wsum, in
   const int w0 = min(words, tid * per), w1 = min(words, w0 + per);
   uint32_t cnt = 0;
   for (int e = w0; e < w1; ++e) cnt += __popc(bitmap[e]);
-  uint32_t inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
+  const uint32_t inc = wave_scan_incl(cnt);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   uint32_t pos = inc - cnt;

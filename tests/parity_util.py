@@ -29,7 +29,7 @@ from compensated_kv_selection_amd import compkv as C
 from compensated_kv_selection_amd.tensors import to_device, torch_to_storage
 from compensated_kv_selection_amd.workloads import DecodeInputs
 from oracle import compkv_oracle as O
-from ws_layout import workspace_regions
+from ws_layout import PUBLISHED_REGIONS, workspace_regions
 
 NEAR_TIE = 1e-5
 OUT_ATOL = 2e-3
@@ -50,16 +50,21 @@ class GpuResult:
 
 
 def check_workspace_clean(ws, dims, budget):
-    """Every call leaves the control words and the fused step's published
-    words (the last two workspace regions) zero, ready for the next call."""
+    """Every call leaves the control words (but each pair's step counter) and
+    the fused step's published headers and candidates zero, ready for the
+    next call."""
     ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
     assert int(ctrl[2]) == 0, "a bounded wait in the step kernel ran out"
+    ctrl = ctrl.clone()
+    ctrl[C.CTRL_WORDS_HEADER + C.CTRL_EPOCH::C.CTRL_WORDS_PER_PAIR] = 0
     assert int(ctrl.abs().sum()) == 0, f"control words not reset: {ctrl.nonzero().flatten().tolist()}"
     regions = workspace_regions(dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim,
                                 dims.max_blocks_per_seq, budget)
     assert sum(regions) == ws.numel(), (sum(regions), ws.numel())
-    tail = ws[sum(regions[:-2]):].view(torch.int64).cpu()
-    assert int((tail != 0).sum()) == 0, "published words not cleared"
+    for r in PUBLISHED_REGIONS:
+        lo = sum(regions[:r])
+        words = ws[lo:lo + regions[r]].view(torch.int64).cpu()
+        assert int((words != 0).sum()) == 0, f"published words of region {r} not cleared"
 
 
 def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.SCORE_COMPKV,

@@ -6,7 +6,8 @@ lie)."""
 def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
     """Region sizes of the sparse-step workspace, each 256-byte aligned:
     control words, per-block scores, chunk partials, select candidates,
-    gather partials, fused chunk headers, fused candidates."""
+    gather partials, fused chunk headers, fused candidates, fused tagged
+    weights, fused partials."""
     def up(x):
         return (x + 255) // 256 * 256
     G = Hq // Hkv
@@ -16,6 +17,10 @@ def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
     kmax = min(max_blocks, budget // 16)
     kcap = max(kmax, 1)
     n_splits = min(64, max(1, (kmax + 3) // 4))
-    return [up((64 + 4 * bg) * 4), up(B * Hq * max_blocks * 4), up(bg * n_chunks * G * pst * 4),
+    return [up((64 + 8 * bg) * 4), up(B * Hq * max_blocks * 4), up(bg * n_chunks * G * pst * 4),
             up(bg * n_slices * kcap * 8), up(bg * n_splits * G * 2 * pst * 4),
-            up(bg * n_chunks * G * 8), up(bg * n_chunks * kcap * 8)]
+            up(bg * n_chunks * G * 8), up(bg * n_chunks * kcap * 8),
+            up(bg * n_chunks * G * 257 * 8), up(bg * 2 * n_chunks * G * (D + 2) * 8)]
+
+
+PUBLISHED_REGIONS = (5, 6)   # fused chunk headers and candidates: zero between calls
