@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "µs per layer decode step & effective HBM GB/s (% peak) at 128K ctx, 512 budget"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ("kernels.hip", "device.hpp", "internal.hpp")
+KERNEL_SOURCES = ("kernels.hip", "fused.hip", "step_common.hpp", "device.hpp", "internal.hpp")
 
 
 def kernel_source_hash() -> str:
@@ -63,6 +63,36 @@ def read_traffic(kernel_tag: str, src_hash: str):
     return float(m_bytes.group(1))
 
 
+def rocprof_summary(directory: str) -> str:
+    """Per-kernel table of the rocprofv3 CSV output (-f csv) under a directory:
+    dispatch counts and durations from *kernel_stats.csv, and the mean per
+    dispatch of each counter in *counter_collection.csv."""
+    import csv
+    import glob
+    from collections import defaultdict
+    lines = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
+        lines.append("|---|---|---|---|---|---|")
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                lines.append(f"| {row['Name'][:90]} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.3f} | "
+                             f"{float(row['MinNs']) / 1e3:.3f} | {float(row['MaxNs']) / 1e3:.3f} | "
+                             f"{float(row['Percentage']):.2f}% |")
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        acc = defaultdict(lambda: [0.0, 0])
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                key = (row["Kernel_Name"][:90], row["Counter_Name"])
+                acc[key][0] += float(row["Counter_Value"])
+                acc[key][1] += 1
+        lines.append("| kernel | counter | dispatches | mean per dispatch |")
+        lines.append("|---|---|---|---|")
+        for (name, counter), (tot, cnt) in sorted(acc.items()):
+            lines.append(f"| {name} | {counter} | {cnt} | {tot / cnt:.1f} |")
+    return "\n".join(lines) if lines else f"no rocprofv3 CSV files under {directory}"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,8 +105,14 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
-                    help="only run a plain device copy of this many MiB (counter calibration)")
+                    help="only run a plain elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--rocprof-summary", default="",
+                    help="only print a per-kernel summary of the rocprofv3 CSV files under this directory")
     args = ap.parse_args()
+
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -98,13 +134,15 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     if args.copy_mb:
+        # torch.neg over fp32: one elementwise kernel that reads n and writes n bytes
         n = args.copy_mb * (1 << 20)
-        x = torch.empty(n, dtype=torch.uint8, device=dev0).fill_(1)
+        x = torch.ones(n // 4, dtype=torch.float32, device=dev0)
         y = torch.empty_like(x)
         for _ in range(5):
-            y.copy_(x)
+            torch.neg(x, out=y)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        print(json.dumps({"copy_kernel": "torch.neg fp32", "read_bytes": n, "write_bytes": n,
+                          "launches": 5}), flush=True)
         return 0
 
     C.load_library()
@@ -174,9 +212,14 @@ def main() -> int:
     wall_s = time.perf_counter() - t0
     region_ms = ev0.elapsed_time(ev1)
     us_per_step = region_ms * 1e3 / args.steps
-    per_launch_us = np.array([us_per_step])
     print(f"[bench] {args.steps} steps (graph replay): {us_per_step:.2f} us/step (events), "
           f"wall {wall_s * 1e6 / args.steps:.1f} us/step", file=sys.stderr, flush=True)
+
+    # The graph holds `steps` back-to-back launches of the step's kernel(s) on
+    # the current stream; the events bracket its replay on that stream.
+    # With three launches per step the three are timed together.
+    launches = C.decode_step_launches(dims, budget)
+    per_launch_us = np.array([us_per_step])
 
     ab = algorithmic_bytes(M, w.num_kv_heads, w.head_dim, w.r_groups, kk, w.block_size, kv_bytes)
     avg_launch_us = float(per_launch_us.mean())
@@ -231,8 +274,11 @@ def main() -> int:
     traffic = read_traffic("decode_step_" + args.workload, src_hash)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": "ckv_step_kernel (one launch per decode step)",
-            "algorithmic_bytes_per_launch": ab["total"], "avg_launch_us": round(avg_launch_us, 3)}
+            "kernel": ("ckv::fused_step_kernel (one launch per decode step)" if launches == 1 else
+                       "ckv::step_kernel x3 (score, select, attend; timed together)"),
+            "algorithmic_bytes_per_launch": ab["total"], "avg_launch_us": round(avg_launch_us, 3),
+            "launch_timing": f"HIP events around a graph replay of {args.steps} steps on the launch stream, "
+                             f"{launches} launch(es) per step"}
     line = {
         "metric": METRIC, "value": round(us_per_step, 3), "unit": "us/step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_per_step / 1e3, 6),

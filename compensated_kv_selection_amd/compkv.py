@@ -27,6 +27,7 @@ EXPORTS = (
     "ckv_score_select",
     "ckv_compensated_decode_attention",
     "ckv_decode_step",
+    "ckv_decode_step_launches",
     "ckv_dense_workspace_bytes",
     "ckv_dense_decode_attention",
     "ckv_status_string",
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ckv_score_select": (I32, [D, P, S, P, P, I32, I32, P, P, P, P, SZ, P]),
         "ckv_compensated_decode_attention": (I32, [D, P, P, P, S, P, P, I32, P, P, I32, P, P, P, SZ, P]),
         "ckv_decode_step": (I32, [D, P, P, P, S, P, P, I32, I32, P, P, P, P, P, SZ, P]),
+        "ckv_decode_step_launches": (I32, [D, I32]),
         "ckv_dense_workspace_bytes": (SZ, [D]),
         "ckv_dense_decode_attention": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "ckv_status_string": (ctypes.c_char_p, [I32]),
@@ -163,6 +165,16 @@ def build_summaries(dims: Dims, k_cache, v_cache, block_table, seq_lens, summari
 def workspace_bytes(dims: Dims, budget_tokens: int) -> int:
     d = dims.c()
     return int(load_library().ckv_workspace_bytes(ctypes.byref(d), budget_tokens))
+
+
+def decode_step_launches(dims: Dims, budget_tokens: int) -> int:
+    """Kernel launches decode_step makes for these dims on the current
+    device: 1 (one persistent launch) or 3 (score, select, attend)."""
+    d = dims.c()
+    n = int(load_library().ckv_decode_step_launches(ctypes.byref(d), budget_tokens))
+    if n == 0:
+        raise ValueError("invalid dims or budget")
+    return n
 
 
 def dense_workspace_bytes(dims: Dims) -> int:

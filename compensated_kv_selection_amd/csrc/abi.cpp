@@ -177,6 +177,19 @@ ckv::Summ to_summ(const ckv_summaries* sm) {
   return ckv::Summ{sm->mean_k, sm->mean_v, sm->gvar, sm->count};
 }
 
+// One launch when its whole grid - at least the two workgroups of every chunk
+// of one (sequence, KV head) pair - can be resident at once and the pair's
+// candidates fit in shared memory; otherwise three launches that never wait.
+// Sets s->bg_round (pairs per round of the persistent grid) when fused.
+bool plan_fused(ckv::Shape* s) {
+  const int resident = ckv::fused_resident_workgroups(*s);
+  const int per_round = resident / (2 * s->n_chunks);
+  if (per_round < 1 || s->share > ckv::kShareMax || s->n_chunks * s->kmax > ckv::kFusedCand) return false;
+  const int bgs = s->B * s->Hkv;
+  s->bg_round = per_round < bgs ? per_round : bgs;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,21 +301,17 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                  num_selected, nullptr, out, lse, score_mode, 1};
   const ckv::Work w = carve(s, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // One launch when its whole grid - at least the two workgroups of every
-  // chunk of one (sequence, KV head) pair - can be resident at once and the
-  // pair's candidates fit in shared memory; otherwise three launches that
-  // never wait.
-  const int resident = ckv::fused_resident_workgroups(s);
-  const int per_round = resident / (2 * s.n_chunks);
-  if (per_round >= 1 && s.share <= ckv::kShareMax && s.n_chunks * s.kmax <= ckv::kFusedCand) {
-    const int bgs = s.B * s.Hkv;
-    s.bg_round = per_round < bgs ? per_round : bgs;
-    return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
-  }
+  if (plan_fused(&s)) return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
   hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
   return hip_status(e, "decode step launches");
+}
+
+int32_t ckv_decode_step_launches(const ckv_dims* dims, int32_t budget_tokens) {
+  ckv::Shape s;
+  if (budget_tokens < 0 || make_shape(dims, budget_tokens, &s) != CKV_OK) return 0;
+  return plan_fused(&s) ? 1 : 3;
 }
 
 size_t ckv_dense_workspace_bytes(const ckv_dims* dims) {

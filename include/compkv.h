@@ -195,6 +195,14 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                            int32_t* num_selected, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Number of kernel launches ckv_decode_step makes for these dims and budget:
+ * 1 when the whole step runs as one persistent launch (every chunk of a
+ * (sequence, KV head) pair resident at once and the pair's candidates fit in
+ * shared memory), 3 otherwise (score, select, attend), 0 if the arguments are
+ * invalid.  Reads the current device's compute-unit count and the kernel's
+ * occupancy on it (3 when no device is present); launches nothing. */
+int32_t ckv_decode_step_launches(const ckv_dims* dims, int32_t budget_tokens);
+
 /* Dense decode attention over every token (the baseline the method is
  * measured against: review "Summary", speed-up over full attention).
  * Workspace from ckv_dense_workspace_bytes, zero-filled before first use

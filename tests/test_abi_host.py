@@ -99,11 +99,14 @@ def test_bad_dims_rejected_everywhere(lib, kw, status, needle):
         assert needle in lib.ckv_last_error().decode()
     assert lib.ckv_workspace_bytes(ctypes.byref(d), 512) == 0
     assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == 0
+    assert lib.ckv_decode_step_launches(ctypes.byref(d), 512) == 0
 
 
 def test_null_dims(lib):
     assert lib.ckv_build_summaries(None, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(summ()), None) == INVALID
     assert lib.ckv_workspace_bytes(None, 512) == 0
+    assert lib.ckv_decode_step_launches(None, 512) == 0
+    assert lib.ckv_decode_step_launches(ctypes.byref(good_dims()), -1) == 0
 
 
 def test_null_pointers_rejected(lib):

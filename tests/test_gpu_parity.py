@@ -6,7 +6,7 @@ import torch
 
 from compensated_kv_selection_amd import compkv as C
 from compensated_kv_selection_amd import workloads as W
-from compensated_kv_selection_amd.tensors import to_device
+from compensated_kv_selection_amd.tensors import dims_of, to_device
 from oracle import compkv_oracle as O
 
 from parity_util import (check_outputs, check_selection_isolated, check_selection_vs_oracle,
@@ -37,6 +37,9 @@ def full_check(w, budget=None, score_mode=C.SCORE_COMPKV, compensate=True, fused
         print(f"[case] {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
               f"d={w.head_dim} r={w.r_groups} {w.dtype} lens={list(w.seq_lens)[:6]} budget={budget} "
               f"mode={score_mode} comp={compensate} fused={fz}", flush=True)
+        if fz:
+            print(f"[case] decode_step launches: {C.decode_step_launches(dims_of(w), budget)}",
+                  flush=True)
         g = run_gpu(w, budget, score_mode, compensate, fused=fz)
         if ora is None:
             ora = run_oracle(w, budget, score_mode, compensate)
@@ -213,6 +216,13 @@ def test_repeat_runs_are_bit_identical():
 
 def test_llama_32k():
     full_check(W.make_preset("llama_32k", seed=0), fused=True)
+
+
+def test_headline_shape_runs_as_one_launch():
+    # 128K tokens, Hq 32, Hkv 8, d 128, 16-token blocks, 512-token budget
+    dims = C.Dims(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, r_groups=4,
+                  num_pages=8192, max_blocks_per_seq=8192, kv_dtype=C.CKV_BF16)
+    assert C.decode_step_launches(dims, 512) == 1
 
 
 def test_llama_128k_headline():
