@@ -178,13 +178,15 @@ ckv::Summ to_summ(const ckv_summaries* sm) {
 }
 
 // One launch when its whole grid - at least the two workgroups of every chunk
-// of one (sequence, KV head) pair - can be resident at once and the pair's
-// candidates fit in shared memory; otherwise three launches that never wait.
+// of one (sequence, KV head) pair - can be resident at once, the pair's
+// candidates fit in shared memory and page ids fit in its selection keys;
+// otherwise three launches that never wait.
 // Sets s->bg_round (pairs per round of the persistent grid) when fused.
 bool plan_fused(ckv::Shape* s) {
   const int resident = ckv::fused_resident_workgroups(*s);
   const int per_round = resident / (2 * s->n_chunks);
   if (per_round < 1 || s->share > ckv::kShareMax || s->n_chunks * s->kmax > ckv::kFusedCand) return false;
+  if (s->P >= (1 << ckv::kFusedPageBits)) return false;
   const int bgs = s->B * s->Hkv;
   s->bg_round = per_round < bgs ? per_round : bgs;
   return true;

@@ -76,6 +76,8 @@ struct CtlLds {
   uint32_t bitmap[kMaxBlocks / 32];
   int pgt[kChunk];        // page of each block of the chunk
   int own[kChunk];        // selected blocks of this chunk (local rows, ascending)
+  int gblk[kShareMax];    // selected blocks this workgroup attends to, and their pages
+  int gpg[kShareMax];
   uint32_t sh[64];
   uint32_t wsum[NW];
   uint32_t count;
@@ -106,6 +108,24 @@ __device__ __forceinline__ uint32_t* ctr_done(const Work& w, int bg) { return w.
 
 __device__ __forceinline__ uint64_t tagged(float x, uint32_t tag) {
   return ((uint64_t)tag << 32) | __float_as_uint(x);
+}
+
+// Candidate keys of the step carry the block's page, so that the workgroup
+// that attends to a selected block needs no page-table read: score bits (32),
+// complemented block index (14), page (18).  They order like make_key - by
+// score, then lower block index first - since distinct blocks differ in the
+// index bits; the page bits never decide.  Real keys are never 0 or 1.
+constexpr uint32_t kNoPage = (1u << kFusedPageBits) - 1;
+__device__ __forceinline__ uint64_t fused_key(float score, int idx, int page) {
+  return ((uint64_t)__float_as_uint(score) << 32) |
+         ((uint64_t)(0x3FFFu - (uint32_t)idx) << kFusedPageBits) | (uint32_t)(page >= 0 ? page : (int)kNoPage);
+}
+__device__ __forceinline__ int fused_key_index(uint64_t key) {
+  return 0x3FFF - (int)((uint32_t)key >> kFusedPageBits);
+}
+__device__ __forceinline__ int fused_key_page(uint64_t key) {
+  const uint32_t p = (uint32_t)key & kNoPage;
+  return p == kNoPage ? -1 : (int)p;
 }
 
 // Copy n published 64-bit words into dst, waiting for each to become
@@ -401,8 +421,9 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   __syncthreads();
 
-  // ---- selection: which blocks of this chunk are attended exactly ----
-  int n_own = 0;
+  // ---- selection: which blocks this workgroup attends to exactly, and
+  // which of the chunk's blocks were selected ----
+  int n_own = 0, n_gather = 0;
   if (ranked) {
     // log Z_hat per head from every chunk header of the pair
     const int nh = s.n_chunks * G;
@@ -432,7 +453,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         const float lam = L.lam[j][i], lz = L.lnz[j];
         if (lam != -INFINITY && lz != -INFINITY) S += expf(lam - lz);
       }
-      L.u.keys[i] = make_key(S, start + i);
+      L.u.keys[i] = fused_key(S, start + i, L.pgt[i]);
     }
     __syncthreads();
     // the chunk's top-k candidates
@@ -458,10 +479,23 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
     for (int e = tid; e < n2; e += NT) {
       const uint64_t key = L.u.keys[e];
-      const int idx = key_index(key);
+      const int idx = fused_key_index(key);
       if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
     }
     __syncthreads();
+    // selected blocks before each bitmap word (words <= 2 NT), into hist
+    {
+      const uint32_t w0 = 2 * tid < words ? L.bitmap[2 * tid] : 0u;
+      const uint32_t w1 = 2 * tid + 1 < words ? L.bitmap[2 * tid + 1] : 0u;
+      const uint32_t c0 = __popc(w0), tot = c0 + __popc(w1);
+      const uint32_t inc = wave_scan_incl(tot);
+      if (lane == 63) L.sh[wave] = inc;
+      __syncthreads();
+      uint32_t off = inc - tot;
+      for (int v = 0; v < wave; ++v) off += L.sh[v];
+      L.hist[2 * tid] = off;
+      L.hist[2 * tid + 1] = off + c0;
+    }
     // this chunk's selected blocks, ascending (kChunk / 32 bitmap words)
     if (wave == 0) {
       const int wd = start / 32 + lane;
@@ -474,14 +508,30 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
     __syncthreads();
     n_own = (int)L.count;
+    // The pair's selected blocks are attended to round robin over its chunks
+    // in ascending order: this workgroup takes ranks chunk, chunk + n_chunks, ...
+    for (int e = tid; e < n2; e += NT) {
+      const uint64_t key = L.u.keys[e];
+      const int idx = fused_key_index(key);
+      if (key >= T && idx >= 0 && idx < M) {
+        const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
+        if (rank % s.n_chunks == chunk) {
+          L.gblk[rank / s.n_chunks] = idx;
+          L.gpg[rank / s.n_chunks] = fused_key_page(key);
+        }
+      }
+    }
+    n_gather = kk > chunk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
+    __syncthreads();
   } else if (kk == M) {
-    // every block selected
-    n_own = nrows;
-    L.own[tid] = tid;
+    // every block selected: each chunk attends to its own
+    n_gather = nrows;
+    L.gblk[tid] = start + tid;
+    L.gpg[tid] = L.pgt[tid];
     __syncthreads();
   }
 
-  // ---- exact attention over the chunk's selected blocks ----
+  // ---- exact attention over this workgroup's share of the selected blocks ----
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -491,9 +541,9 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
   {
-    // one batch covers UG tokens per row slot (8 blocks per workgroup); all
-    // its loads, and those of the take-back rows, are issued together
-    constexpr int UG = 8;
+    // one batch covers UG tokens per row slot (RS * UG tokens), all its loads
+    // issued together
+    constexpr int UG = 4;
     const KV* kc = static_cast<const KV*>(io.k_cache);
     const KV* vc = static_cast<const KV*>(io.v_cache);
     float qv[G][8];
@@ -501,41 +551,38 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     for (int j = 0; j < G; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[j][e] = L.qf[j * D + c * 8 + e];
-    const int ntok = n_own * kBlockSize;
+    const int ntok = n_gather * kBlockSize;
     // The value workgroup sums the compensation terms of every block of the
-    // chunk; the terms of the selected ones are taken back here, as the
-    // starting state (frame: the chunk max) of the exact softmax.
+    // chunk; the terms of the chunk's selected blocks are taken back here,
+    // before any exact term, in the frame of the chunk max.
     const bool take_back = comp && n_own > 0;
     if (take_back) {
 #pragma unroll
       for (int j = 0; j < G; ++j) m[j] = L.mx[j];
     }
-    for (int t0 = 0; t0 < max(ntok, take_back ? n_own : 0); t0 += RS * UG) {
+    for (int t0 = 0; t0 < max(ntok, take_back ? 1 : 0); t0 += RS * UG) {
       Raw8<KV> kr[UG], vr[UG];
       bool ok[UG];
 #pragma unroll
       for (int u = 0; u < UG; ++u) {
         const int R = t0 + u * RS + rs;
-        const int ri = R < ntok ? L.own[R / kBlockSize] : 0, tok = R % kBlockSize;
-        const int pg = L.pgt[ri];
-        ok[u] = R < ntok && pg >= 0 && tok < Lseq - (start + ri) * s.bs;
+        const int gi = R < ntok ? R / kBlockSize : 0, tok = R % kBlockSize;
+        const int blk = L.gblk[gi], pg = L.gpg[gi];
+        ok[u] = R < ntok && pg >= 0 && tok < Lseq - blk * s.bs;
         if (ok[u]) {
           const size_t off = (((size_t)pg * s.Hkv + g) * s.bs + tok) * D + c * 8;
           raw_load(kc + off, kr[u]);
           raw_load(vc + off, vr[u]);
         }
       }
-      if (take_back) {
-        // the selected rows' mean values: row slot rs takes rows e = t0/16 + rs, ...
-        // The weights are in the chunk-max frame; earlier batches may have
-        // raised the row's running max above it.
-        for (int e = t0 / kBlockSize + rs; e < min(n_own, (t0 + RS * UG) / kBlockSize); e += RS) {
+      if (t0 == 0 && take_back) {
+        for (int e = rs; e < n_own; e += RS) {
           const int ri = L.own[e];
           float nv[8];
           load8(mv + (size_t)ri * D + c * 8, nv);
 #pragma unroll
           for (int j = 0; j < G; ++j) {
-            const float wt = L.wt[j][ri] * (t0 == 0 ? 1.f : expf(L.mx[j] - m[j]));
+            const float wt = L.wt[j][ri];
             l[j] -= wt;
 #pragma unroll
             for (int e2 = 0; e2 < 8; ++e2) acc[j][e2] = fmaf(-wt, nv[e2], acc[j][e2]);

@@ -21,6 +21,7 @@ constexpr int kCandLds = 2048;      // second-level candidates kept in LDS (else
 constexpr int kShareMax = 256;      // selected blocks one fused workgroup attends to
 constexpr int kMaxChunks = (kMaxBlocks + kChunk - 1) / kChunk;
 constexpr int kFusedCand = 4608;    // fused step: candidates of all chunks held in LDS
+constexpr int kFusedPageBits = 18;  // fused step: page ids carried in selection keys (P < 2^18)
 constexpr int kPartStride(int d) { return d + 4; }  // [m, l, z, c, acc[d]]
 constexpr int kCtrlHeader = 64;     // uint32 words before the per-(sequence, KV head) counters
 constexpr int kCtrlPerPair = 8;     // control words per (sequence, KV head)
