@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/compkv.h"
@@ -74,6 +75,7 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.n_slices = (x.max_blocks + ckv::kSlice - 1) / ckv::kSlice;
   x.share = x.kmax > 0 ? (x.kmax + x.n_chunks - 1) / x.n_chunks : 1;
   x.bg_round = 0;
+  x.n_xcd = 0;
   int splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
   splits = splits < 1 ? 1 : (splits > ckv::kMaxSplits ? ckv::kMaxSplits : splits);
   x.n_splits = splits;
@@ -182,13 +184,27 @@ ckv::Summ to_summ(const ckv_summaries* sm) {
 // candidates fit in shared memory and page ids fit in its selection keys;
 // otherwise three launches that never wait.
 // Sets s->bg_round (pairs per round of the persistent grid) when fused.
-bool plan_fused(ckv::Shape* s) {
+// When blocks go to the device's XCDs round robin (checked once per device,
+// not while `stream` is capturing) and the workgroups of one pair fit on one
+// XCD at once, every pair is kept on one XCD (s->n_xcd set), so that its
+// workgroups hand data to each other through that XCD's L2.
+bool plan_fused(ckv::Shape* s, hipStream_t stream, bool probe) {
   const int resident = ckv::fused_resident_workgroups(*s);
   const int per_round = resident / (2 * s->n_chunks);
   if (per_round < 1 || s->share > ckv::kShareMax || s->n_chunks * s->kmax > ckv::kFusedCand) return false;
   if (s->P >= (1 << ckv::kFusedPageBits)) return false;
   const int bgs = s->B * s->Hkv;
   s->bg_round = per_round < bgs ? per_round : bgs;
+  s->n_xcd = 0;
+  const char* off = getenv("CKV_FUSED_ACROSS_XCDS");
+  const int nx = probe && !(off && off[0] == '1') ? ckv::fused_xcd_count(stream) : 0;
+  if (nx > 0) {
+    const int per_xcd = resident / nx / (2 * s->n_chunks);  // pairs one XCD holds at once
+    if (per_xcd >= 1) {
+      s->n_xcd = nx;
+      s->bg_round = nx * per_xcd < bgs ? nx * per_xcd : bgs;
+    }
+  }
   return true;
 }
 
@@ -303,7 +319,7 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                  num_selected, nullptr, out, lse, score_mode, 1};
   const ckv::Work w = carve(s, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (plan_fused(&s)) return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
+  if (plan_fused(&s, st, true)) return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
   hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
@@ -313,7 +329,7 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
 int32_t ckv_decode_step_launches(const ckv_dims* dims, int32_t budget_tokens) {
   ckv::Shape s;
   if (budget_tokens < 0 || make_shape(dims, budget_tokens, &s) != CKV_OK) return 0;
-  return plan_fused(&s) ? 1 : 3;
+  return plan_fused(&s, nullptr, false) ? 1 : 3;
 }
 
 size_t ckv_dense_workspace_bytes(const ckv_dims* dims) {

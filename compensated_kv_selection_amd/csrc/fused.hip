@@ -42,6 +42,7 @@
 // host launches it only when the whole grid can be resident, so the
 // workgroups of a pair can wait for each other.  Every wait is bounded and
 // sets the error word when it runs out.
+#include <atomic>
 #include <type_traits>
 
 #include "step_common.hpp"
@@ -55,6 +56,7 @@ constexpr int NW = NT / 64;                // waves per workgroup
 constexpr int kPollBatch = 8;              // published words read per thread per round trip
 constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
 constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
+constexpr int kXccProbeBlocks = 256;       // workgroups of the XCD placement check
 
 template <int D, int G>
 struct CtlLds {
@@ -394,8 +396,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 
   // ---- per head: chunk max, Z_hat part, compensation weights, log-scores ----
   if (need_mu) {
-    const Coh hdr(w.fhdr + (size_t)bg * s.n_chunks * G, (size_t)s.n_chunks * G * 8);
-    const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8);
+    const Coh hdr(w.fhdr + (size_t)bg * s.n_chunks * G, (size_t)s.n_chunks * G * 8, s.n_xcd > 0);
+    const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8, s.n_xcd > 0);
     for (int j = wave; j < G; j += NW) {
       float mx = -INFINITY;
       for (int ri = lane; ri < nrows; ri += 64) mx = fmaxf(mx, L.sb[j][ri]);
@@ -428,7 +430,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     // log Z_hat per head from every chunk header of the pair
     const int nh = s.n_chunks * G;
     {
-      const Coh hdr(w.fhdr + (size_t)bg * nh, (size_t)nh * 8);
+      const Coh hdr(w.fhdr + (size_t)bg * nh, (size_t)nh * 8, s.n_xcd > 0);
       read_published(hdr, nh, nh, 0, L.u.keys, err);
     }
     __syncthreads();
@@ -457,7 +459,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
     __syncthreads();
     // the chunk's top-k candidates
-    const Coh cand(w.fcand + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8);
+    const Coh cand(w.fcand + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8, s.n_xcd > 0);
     const int k1 = min(kk, nrows);
     if (k1 > 0) {
       const uint64_t T1 = k1 == nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
@@ -602,7 +604,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       }
     }
   }
-  const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + chunk) * G * (D + 2), (size_t)G * (D + 2) * 8);
+  const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + chunk) * G * (D + 2), (size_t)G * (D + 2) * 8,
+                 s.n_xcd > 0);
   publish_partial<D, G>(m, l, acc, L.u.red, part, tag);
 
   // ---- the selection outputs ----
@@ -648,7 +651,7 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
   if (comp) {
-    const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8);
+    const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8, s.n_xcd > 0);
     uint32_t spins = 0;
     // the chunk maxima come last from the control workgroup: once they are
     // here, its mean keys have arrived and the mean values may stream
@@ -685,7 +688,7 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
   }
   const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
-                 (size_t)G * (D + 2) * 8);
+                 (size_t)G * (D + 2) * 8, s.n_xcd > 0);
   publish_partial<D, G>(m, l, acc, L.red, part, tag);
 }
 
@@ -707,7 +710,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   const int per = (NV + np - 1) / np;  // float4 outputs of this workgroup
   const int step = max(1, NT / np);    // outputs merged per pass
   const int o0 = slot * per, o1 = min(NV, o0 + per);
-  const Coh part(w.fpart + (size_t)bg * np * G * (D + 2), (size_t)np * G * (D + 2) * 8);
+  const Coh part(w.fpart + (size_t)bg * np * G * (D + 2), (size_t)np * G * (D + 2) * 8, s.n_xcd > 0);
   uint32_t spins = 0;
   for (int base = o0; base < o1; base += step) {
     // the (output, partial) items of this pass: six words each, read together
@@ -772,9 +775,9 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   const int kk = min(M, s.kmax);
   if (kk > 0 && kk < M) {
     const int nch = s.n_chunks;
-    const Coh hdr(w.fhdr + (size_t)bg * nch * G, (size_t)nch * G * 8);
+    const Coh hdr(w.fhdr + (size_t)bg * nch * G, (size_t)nch * G * 8, s.n_xcd > 0);
     for (int e = tid; e < nch * G; e += NT) hdr.put_u64(e, 0u);
-    const Coh cand(w.fcand + (size_t)bg * nch * s.kmax, (size_t)nch * s.kmax * 8);
+    const Coh cand(w.fcand + (size_t)bg * nch * s.kmax, (size_t)nch * s.kmax * 8, s.n_xcd > 0);
     for (int e = tid; e < nch * kk; e += NT) cand.put_u64((e / kk) * s.kmax + e % kk, 0u);
   }
   if (tid == 0) {
@@ -787,11 +790,25 @@ template <typename KV, int D, int G>
 __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
   __shared__ FusedLds<D, G> lds;
   __shared__ uint32_t sh[4];
-  const int half = s.bg_round * s.n_chunks;
-  const bool ctl = (int)blockIdx.x < half;
-  const int t = ctl ? (int)blockIdx.x : (int)blockIdx.x - half;
-  const int chunk = t % s.n_chunks;
-  for (int bg = t / s.n_chunks; bg < s.B * s.Hkv; bg += s.bg_round) {
+  // This workgroup's pair (of the round), role and chunk.  Kept on one XCD
+  // (n_xcd > 0): workgroup i runs on XCD i % n_xcd, which takes the pairs
+  // p = XCD, XCD + n_xcd, ...; otherwise control workgroups come first.
+  int pair, role;
+  if (s.n_xcd > 0) {
+    const int slot = (int)blockIdx.x / s.n_xcd;
+    pair = (int)blockIdx.x % s.n_xcd + s.n_xcd * (slot / (2 * s.n_chunks));
+    role = slot % (2 * s.n_chunks);
+    if (pair >= s.bg_round) return;
+  } else {
+    const int half = s.bg_round * s.n_chunks;
+    const bool c = (int)blockIdx.x < half;
+    const int t = c ? (int)blockIdx.x : (int)blockIdx.x - half;
+    pair = t / s.n_chunks;
+    role = (c ? 0 : s.n_chunks) + t % s.n_chunks;
+  }
+  const bool ctl = role < s.n_chunks;
+  const int chunk = role % s.n_chunks;
+  for (int bg = pair; bg < s.B * s.Hkv; bg += s.bg_round) {
     const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
     if (ctl) ctl_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.c);
     else val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
@@ -840,8 +857,44 @@ int fused_resident_workgroups(const Shape& s) {
   });
 }
 
+__device__ uint32_t g_xcc_of_block[kXccProbeBlocks];
+
+__global__ void xcc_probe_kernel() {
+  if (threadIdx.x == 0) {
+    uint32_t id;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(id));
+    g_xcc_of_block[blockIdx.x] = id;
+  }
+}
+
+int fused_xcd_count(hipStream_t st) {
+  constexpr int kDevices = 64;
+  static std::atomic<int> known[kDevices];  // 0 unknown, -1 not round robin, else XCDs
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
+  const int k = known[dev].load(std::memory_order_relaxed);
+  if (k != 0) return k > 0 ? k : 0;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 0;
+  uint32_t ids[kXccProbeBlocks];
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(kXccProbeBlocks), dim3(64), 0, st);
+  if (hipGetLastError() != hipSuccess ||
+      hipMemcpyFromSymbolAsync(ids, HIP_SYMBOL(g_xcc_of_block), sizeof ids, 0, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  uint32_t n = 0;
+  for (int i = 0; i < kXccProbeBlocks; ++i) n = ids[i] + 1 > n ? ids[i] + 1 : n;
+  bool rr = n >= 1 && n <= 16;
+  for (int i = 0; rr && i < kXccProbeBlocks; ++i) rr = ids[i] == (uint32_t)i % n;
+  known[dev].store(rr ? (int)n : -1, std::memory_order_relaxed);
+  return rr ? (int)n : 0;
+}
+
 hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t st) {
-  const dim3 grid(2 * s.bg_round * s.n_chunks);
+  const dim3 grid(s.n_xcd > 0 ? s.n_xcd * ((s.bg_round + s.n_xcd - 1) / s.n_xcd) * 2 * s.n_chunks
+                              : 2 * s.bg_round * s.n_chunks);
   return with_fused(s, [&](auto fn, int) {
     hipLaunchKernelGGL(fn, grid, dim3(NT), 0, st, s, io, w);
     return hipGetLastError();

@@ -45,6 +45,7 @@ struct Shape {
   int n_slices;       // select workgroups per (sequence, KV head)
   int share;          // selected blocks attended by one chunk workgroup (fused)
   int bg_round;       // (sequence, KV head) pairs processed at once by the fused grid
+  int n_xcd;          // fused: > 0 = XCDs of the device, each pair kept on one XCD; 0 = spread
   int n_splits;       // gather workgroups per (sequence, KV head) (attend-only, dense)
   int pages_per_split;
   int dtype;          // 0 = bf16, 1 = f32
@@ -106,7 +107,14 @@ hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w
 int fused_resident_workgroups(const Shape& s);
 
 // One launch of the fused step kernel; s.bg_round must be set, with
-// s.bg_round * s.n_chunks <= fused_resident_workgroups(s).
+// s.bg_round * s.n_chunks <= fused_resident_workgroups(s), and with n_xcd > 0
+// ceil(bg_round / n_xcd) * 2 * n_chunks <= fused_resident_workgroups(s) / n_xcd.
 hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t stream);
+
+// Number of XCDs if the device sends workgroup i of a launch to XCD
+// i % (number of XCDs), else 0.  Checked once per device with a small kernel
+// on `stream` (waits for it); returns 0 without checking while `stream` is
+// capturing a graph.
+int fused_xcd_count(hipStream_t stream);
 
 }  // namespace ckv

@@ -43,12 +43,18 @@ constexpr int kSc1 = 16;                // cache-policy operand: device scope
 
 // A buffer view of `bytes` bytes at `base`; element indices are in units of
 // the accessed type.  Accesses past `bytes` read 0 and drop writes.
+// With `local` set, 64-bit words are stored with the default policy: they
+// stay in the writer's L2, where device-scope loads from workgroups on the
+// same XCD find them (much sooner than a write-through store reaches memory);
+// workgroups on other XCDs may not see them before the launch ends.
 struct Coh {
   __amdgpu_buffer_rsrc_t r;
-  __device__ Coh(const void* base, size_t bytes)
+  bool local;
+  __device__ Coh(const void* base, size_t bytes, bool local_ = false)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                             (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
-                                            kRsrcWord3)) {}
+                                            kRsrcWord3)),
+        local(local_) {}
   __device__ float f32(int i) const {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * i, 0, kSc1));
   }
@@ -74,7 +80,8 @@ struct Coh {
     u32x2_t w;
     w.x = (uint32_t)v;
     w.y = (uint32_t)(v >> 32);
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, 8 * i, 0, kSc1);
+    if (local) __builtin_amdgcn_raw_buffer_store_b64(w, r, 8 * i, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b64(w, r, 8 * i, 0, kSc1);
   }
 };
 

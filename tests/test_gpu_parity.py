@@ -218,6 +218,17 @@ def test_llama_32k():
     full_check(W.make_preset("llama_32k", seed=0), fused=True)
 
 
+@pytest.mark.parametrize("across_xcds", [False, True])
+def test_fused_step_both_placements(across_xcds, monkeypatch):
+    # By default a pair's workgroups share one XCD and hand data over through
+    # its L2; CKV_FUSED_ACROSS_XCDS=1 spreads them and uses device-scope
+    # stores.  Both must match the oracle.
+    if across_xcds:
+        monkeypatch.setenv("CKV_FUSED_ACROSS_XCDS", "1")
+    full_check(small_gqa(seed=4), fused=True)
+    full_check(W.make_preset("llama_32k", seed=3), fused=True)
+
+
 def test_headline_shape_runs_as_one_launch():
     # 128K tokens, Hq 32, Hkv 8, d 128, 16-token blocks, 512-token budget
     dims = C.Dims(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, r_groups=4,
