@@ -83,6 +83,9 @@ struct CtlLds {
   uint32_t sh[64];
   uint32_t wsum[NW];
   uint32_t count;
+  uint64_t tlo;           // lower bound of the pair's k-th largest candidate
+  uint64_t surv[64];      // candidates at or above it
+  uint32_t nown;          // selected blocks of this chunk
 };
 
 template <int D, int G>
@@ -426,6 +429,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   // ---- selection: which blocks this workgroup attends to exactly, and
   // which of the chunk's blocks were selected ----
   int n_own = 0, n_gather = 0;
+  bool listed = false;  // selection list (and output) made by the one-wave path
   if (ranked) {
     // log Z_hat per head from every chunk header of the pair
     const int nh = s.n_chunks * G;
@@ -447,84 +451,159 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       if (lane == 0) L.lnz[j] = zs > 0.f ? mz + logf(zs) : -INFINITY;
     }
     __syncthreads();
-    // ranked score of each block of the chunk
-    for (int i = tid; i < nrows; i += NT) {
+    // ranked score of block tid of the chunk (nrows <= NT)
+    uint64_t mykey = 0;
+    if (tid < nrows) {
       float S = 0.f;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const float lam = L.lam[j][i], lz = L.lnz[j];
+        const float lam = L.lam[j][tid], lz = L.lnz[j];
         if (lam != -INFINITY && lz != -INFINITY) S += expf(lam - lz);
       }
-      L.u.keys[i] = fused_key(S, start + i, L.pgt[i]);
+      mykey = fused_key(S, start + tid, L.pgt[tid]);
     }
-    __syncthreads();
-    // the chunk's top-k candidates
+    // the chunk's top-k candidates, published largest first
     const Coh cand(w.fcand + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8, s.n_xcd > 0);
     const int k1 = min(kk, nrows);
-    if (k1 > 0) {
-      const uint64_t T1 = k1 == nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
-      if (tid == 0) L.count = 0u;
+    const bool fast = kk <= 64;  // selections of up to one wave's width stay in registers
+    if (fast) {
+      // each wave sorts its 64 blocks; wave 0 merges the four lists
+      const uint64_t srt = wave_sort_desc(mykey);
+      L.u.keys[tid] = srt;
       __syncthreads();
-      for (int i = tid; i < nrows; i += NT) {
-        const uint64_t key = L.u.keys[i];
-        if (key >= T1) cand.put_u64(chunk * s.kmax + (int)atomicAdd(&L.count, 1u), key);
+      if (wave == 0) {
+        uint64_t top = srt;
+        for (int v = 1; v < NW; ++v) top = wave_merge_desc(top, L.u.keys[64 * v + 63 - lane]);
+        if (lane < kk) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
       }
+    } else {
+      if (tid < nrows) L.u.keys[tid] = mykey;
+      __syncthreads();
+      if (k1 > 0) {
+        const uint64_t T1 = k1 == nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
+        if (tid == 0) L.count = 0u;
+        __syncthreads();
+        for (int i = tid; i < nrows; i += NT) {
+          const uint64_t key = L.u.keys[i];
+          if (key >= T1) cand.put_u64(chunk * s.kmax + (int)atomicAdd(&L.count, 1u), key);
+        }
+      }
+      for (int e = k1 + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);  // below every real key
     }
-    for (int e = k1 + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);  // below every real key
     __syncthreads();
     // the pair's top-k from every chunk's candidates
     const int n2 = s.n_chunks * kk;
     read_published(cand, n2, kk, s.kmax, L.u.keys, err);
-    const int words = (M + 31) / 32;
-    for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
     __syncthreads();
-    const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
-    for (int e = tid; e < n2; e += NT) {
-      const uint64_t key = L.u.keys[e];
-      const int idx = fused_key_index(key);
-      if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
-    }
-    __syncthreads();
-    // selected blocks before each bitmap word (words <= 2 NT), into hist
-    {
-      const uint32_t w0 = 2 * tid < words ? L.bitmap[2 * tid] : 0u;
-      const uint32_t w1 = 2 * tid + 1 < words ? L.bitmap[2 * tid + 1] : 0u;
-      const uint32_t c0 = __popc(w0), tot = c0 + __popc(w1);
-      const uint32_t inc = wave_scan_incl(tot);
-      if (lane == 63) L.sh[wave] = inc;
-      __syncthreads();
-      uint32_t off = inc - tot;
-      for (int v = 0; v < wave; ++v) off += L.sh[v];
-      L.hist[2 * tid] = off;
-      L.hist[2 * tid + 1] = off + c0;
-    }
-    // this chunk's selected blocks, ascending (kChunk / 32 bitmap words)
-    if (wave == 0) {
-      const int wd = start / 32 + lane;
-      const uint32_t bits = (lane < kChunk / 32 && wd < words) ? L.bitmap[wd] : 0u;
-      const uint32_t cnt = __popc(bits);
-      const uint32_t inc = wave_scan_incl(cnt);
-      uint32_t pos = inc - cnt;
-      for (uint32_t x = bits; x; x &= x - 1) L.own[pos++] = 32 * lane + __ffs(x) - 1;
-      if (lane == 63) L.count = inc;
-    }
-    __syncthreads();
-    n_own = (int)L.count;
-    // The pair's selected blocks are attended to round robin over its chunks
-    // in ascending order: this workgroup takes ranks chunk, chunk + n_chunks, ...
-    for (int e = tid; e < n2; e += NT) {
-      const uint64_t key = L.u.keys[e];
-      const int idx = fused_key_index(key);
-      if (key >= T && idx >= 0 && idx < M) {
-        const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
-        if (rank % s.n_chunks == chunk) {
-          L.gblk[rank / s.n_chunks] = idx;
-          L.gpg[rank / s.n_chunks] = fused_key_page(key);
+    if (fast) {
+      // A lower bound of the k-th largest candidate: the k-th largest of the
+      // first m candidates of every chunk (at most 64 keys).  The keys at or
+      // above it hold the top k; when they fit in one wave they are sorted
+      // there, then re-sorted by block index, which gives every block's rank.
+      if (wave == 0) {
+        const int m = min(kk, max(1, 64 / s.n_chunks));
+        const int c = lane / m, e = lane % m;
+        const uint64_t v = c < s.n_chunks ? L.u.keys[c * kk + e] : 0ull;
+        const uint64_t srt = wave_sort_desc(v);
+        const int kth = s.n_chunks * m >= kk ? kk - 1 : 63;  // too few keys: no bound (lane 63 holds 0)
+        const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)srt, kth);
+        const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(srt >> 32), kth);
+        if (lane == 0) {
+          L.tlo = (hi << 32) | lo;
+          L.count = 0u;
         }
       }
+      __syncthreads();
+      const uint64_t tlo = L.tlo;
+      for (int e = tid; e < n2; e += NT) {
+        const uint64_t key = L.u.keys[e];
+        if (key >= tlo) {
+          const uint32_t pos = atomicAdd(&L.count, 1u);
+          if (pos < 64) L.surv[pos] = key;
+        }
+      }
+      __syncthreads();
+      const uint32_t nsurv = L.count;
+      if (nsurv <= 64) {
+        listed = true;
+        if (wave == 0) {
+          const uint64_t top = wave_sort_desc(lane < (int)nsurv ? L.surv[lane] : 0ull);
+          const int ti = fused_key_index(top);
+          const bool sel = lane < kk && ti >= 0 && ti < M;
+          // by block index, ascending: sort on the complemented index
+          const uint64_t a = wave_sort_desc(sel ? ((uint64_t)(0x3FFFu - (uint32_t)ti) << 32) |
+                                                      (uint32_t)fused_key_page(top)
+                                                : 0ull);
+          const bool real = (a >> 32) != 0;
+          const int bi = 0x3FFF - (int)(a >> 32), bp = (int)(uint32_t)a;
+          // lane e < kk holds the e-th selected block of the pair
+          if (real && lane % s.n_chunks == chunk) {
+            L.gblk[lane / s.n_chunks] = bi;
+            L.gpg[lane / s.n_chunks] = bp;
+          }
+          const bool mine = real && bi >= start && bi < start + nrows;
+          const uint64_t mb = __ballot(mine);
+          if (mine) L.own[__popcll(mb & ((1ull << lane) - 1ull))] = bi - start;
+          if (lane == 0) L.nown = (uint32_t)__popcll(mb);
+          if (chunk == 0 && io.selected && lane < kk) io.selected[(size_t)bg * s.kmax + lane] = real ? bi : -1;
+        }
+        __syncthreads();
+        n_own = (int)L.nown;
+        n_gather = kk > chunk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
+      }
     }
-    n_gather = kk > chunk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
-    __syncthreads();
+    if (!listed) {
+      const int words = (M + 31) / 32;
+      for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
+      __syncthreads();
+      const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
+      for (int e = tid; e < n2; e += NT) {
+        const uint64_t key = L.u.keys[e];
+        const int idx = fused_key_index(key);
+        if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
+      }
+      __syncthreads();
+      // selected blocks before each bitmap word (words <= 2 NT), into hist
+      {
+        const uint32_t w0 = 2 * tid < words ? L.bitmap[2 * tid] : 0u;
+        const uint32_t w1 = 2 * tid + 1 < words ? L.bitmap[2 * tid + 1] : 0u;
+        const uint32_t c0 = __popc(w0), tot = c0 + __popc(w1);
+        const uint32_t inc = wave_scan_incl(tot);
+        if (lane == 63) L.sh[wave] = inc;
+        __syncthreads();
+        uint32_t off = inc - tot;
+        for (int v = 0; v < wave; ++v) off += L.sh[v];
+        L.hist[2 * tid] = off;
+        L.hist[2 * tid + 1] = off + c0;
+      }
+      // this chunk's selected blocks, ascending (kChunk / 32 bitmap words)
+      if (wave == 0) {
+        const int wd = start / 32 + lane;
+        const uint32_t bits = (lane < kChunk / 32 && wd < words) ? L.bitmap[wd] : 0u;
+        const uint32_t cnt = __popc(bits);
+        const uint32_t inc = wave_scan_incl(cnt);
+        uint32_t pos = inc - cnt;
+        for (uint32_t x = bits; x; x &= x - 1) L.own[pos++] = 32 * lane + __ffs(x) - 1;
+        if (lane == 63) L.count = inc;
+      }
+      __syncthreads();
+      n_own = (int)L.count;
+      // The pair's selected blocks are attended to round robin over its chunks
+      // in ascending order: this workgroup takes ranks chunk, chunk + n_chunks, ...
+      for (int e = tid; e < n2; e += NT) {
+        const uint64_t key = L.u.keys[e];
+        const int idx = fused_key_index(key);
+        if (key >= T && idx >= 0 && idx < M) {
+          const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
+          if (rank % s.n_chunks == chunk) {
+            L.gblk[rank / s.n_chunks] = idx;
+            L.gpg[rank / s.n_chunks] = fused_key_page(key);
+          }
+        }
+      }
+      n_gather = kk > chunk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
+      __syncthreads();
+    }
   } else if (kk == M) {
     // every block selected: each chunk attends to its own
     n_gather = nrows;
@@ -614,8 +693,9 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     if (tid == 0 && io.num_selected) io.num_selected[bg] = kk;
     if (out) {
       for (int e = kk + tid; e < s.kmax; e += NT) out[e] = -1;
-      if (ranked) emit_selection<NT>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
-      else
+      if (ranked) {
+        if (!listed) emit_selection<NT>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
+      } else
         for (int i = tid; i < kk; i += NT) out[i] = i;
     }
   }

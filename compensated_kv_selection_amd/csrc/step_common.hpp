@@ -324,6 +324,68 @@ __device__ uint64_t radix_kth_largest(const KeyAt key_at, int n, int k, uint32_t
   return prefix;
 }
 
+// ---- wave-wide sorting of 64-bit keys, one per lane ----------------------------
+// Value of lane (lane ^ J) for J = 1, 2, 4, 8 (DPP within a row of 16 lanes;
+// row_ror:n brings lane (i - n) mod 16) and 16, 32 (permlane swaps, which
+// return the even/odd row, resp. low/high half, of each pair).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const uint32_t lane = __lane_id();
+  if constexpr (J == 1) {
+    return dpp_quad_xor1(x);
+  } else if constexpr (J == 2) {
+    return dpp_quad_xor2(x);
+  } else if constexpr (J == 4) {
+    const uint32_t below = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false);  // i - 4
+    const uint32_t above = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x12C, 0xF, 0xF, false);  // i + 4
+    return (lane & 4u) ? below : above;
+  } else if constexpr (J == 8) {
+    return dpp_row_ror8(x);
+  } else if constexpr (J == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16u) ? (uint32_t)p[0] : (uint32_t)p[1];
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32u) ? (uint32_t)h[0] : (uint32_t)h[1];
+  }
+}
+
+// Compare-exchange with lane ^ J: this lane keeps the larger key if
+// keep_max, else the smaller.
+template <int J>
+__device__ __forceinline__ uint64_t cmpx(uint64_t k, bool keep_max) {
+  const uint64_t o = ((uint64_t)lane_xor<J>((uint32_t)(k >> 32)) << 32) | lane_xor<J>((uint32_t)k);
+  return (k > o) == keep_max ? k : o;
+}
+
+// Bitonic merge steps J, J/2, ..., 1 of stage K (K = 64: the final,
+// descending stage).  Runs of K lanes alternate direction below K = 64.
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_steps(uint64_t k) {
+  const uint32_t lane = __lane_id();
+  k = cmpx<J>(k, ((lane & (uint32_t)K) == 0) == ((lane & (uint32_t)J) == 0));
+  if constexpr (J > 1) return bitonic_steps<K, J / 2>(k);
+  else return k;
+}
+
+// The 64 keys of the wave, one per lane, sorted in descending order across
+// lanes (lane 0 the largest).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t k) {
+  k = bitonic_steps<2, 1>(k);
+  k = bitonic_steps<4, 2>(k);
+  k = bitonic_steps<8, 4>(k);
+  k = bitonic_steps<16, 8>(k);
+  k = bitonic_steps<32, 16>(k);
+  return bitonic_steps<64, 32>(k);
+}
+
+// Two descending 64-key lists, a in lane order and b in reversed lane order
+// (lane i holds b[63 - i]): the 64 largest of their union, descending.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b_reversed) {
+  return bitonic_steps<64, 32>(a > b_reversed ? a : b_reversed);
+}
+
 // Walk the selection bitmap (M bits) in ascending block order.  Writes the
 // first `cap` entries of the ascending list to `out` when given, and the
 // blocks at list positions [share_lo, share_hi) to share[0..).  wsum: NT/64
