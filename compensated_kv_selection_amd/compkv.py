@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 LIB_NAME = "libcompkv.so"
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+# The in-tree build; CKV_LIBRARY names another build of the same library.
+LIB_PATH = os.environ.get("CKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 CKV_BF16, CKV_F32 = 0, 1
 SCORE_COMPKV, SCORE_MASS = 0, 1

@@ -866,10 +866,25 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   }
 }
 
+// Brings every 64-byte line of the kernel's explicit arguments into the
+// scalar cache with one round of independent loads.  Left to itself the
+// compiler loads arguments where they are first used, behind branches on
+// other arguments, which costs one memory round trip per line.
+__device__ __forceinline__ void warm_kernel_args() {
+  typedef const __attribute__((address_space(4))) uint32_t* KArg;
+  const KArg ka = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int kBytes = (int)(sizeof(Shape) + sizeof(StepIO) + sizeof(Work));
+  uint32_t x = 0;
+#pragma unroll
+  for (int o = 0; o < kBytes; o += 64) x ^= ka[o / 4];
+  asm volatile("" ::"s"(x));
+}
+
 template <typename KV, int D, int G>
 __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
   __shared__ FusedLds<D, G> lds;
   __shared__ uint32_t sh[4];
+  warm_kernel_args();
   // This workgroup's pair (of the round), role and chunk.  Kept on one XCD
   // (n_xcd > 0): workgroup i runs on XCD i % n_xcd, which takes the pairs
   // p = XCD, XCD + n_xcd, ...; otherwise control workgroups come first.
