@@ -20,23 +20,27 @@
 //     publishes the chunk's compensation weights and header (max logit,
 //     partial Z_hat per head), reads every header of the pair, ranks the
 //     chunk's blocks, publishes the chunk's top-k candidates, reads every
-//     candidate of the pair, finds the pair's top-k, attends exactly to the
-//     selected blocks that lie in its chunk and takes back their
-//     compensation terms;
+//     candidate of the pair, finds the pair's top-k, attends exactly to its
+//     share of the selected blocks (ranks chunk, chunk + n_chunks, ... of the
+//     pair's selection), takes back the compensation terms of the selected
+//     blocks of its chunk, folds in the value workgroup's sums and publishes
+//     one (max, sum, acc[d]) partial per query head;
 //   a value workgroup waits for the chunk's weights, streams the chunk's mean
 //     values and sums the compensation terms of all the chunk's blocks.
+// Then every workgroup of the pair merges its slice of the pair's output from
+// the control workgroups' partials; the last to finish clears the pair's
+// headers and candidates and advances its epoch.
 // A wave's memory counter drains in issue order, so the long mean-value
 // stream lives in workgroups that never wait on small hand-offs, and it
 // starts once the mean keys have arrived, so that the ranking does not wait
 // behind it.
-// Hand-offs go through device-coherent (sc1) memory.  Headers and candidates
-// are 64-bit words that are never 0 once written (cleared after use);
-// weights and partials carry the call's epoch in their upper half.  Readers
-// poll such words directly, so publishing needs no completion wait.  Each
-// workgroup publishes one (max, sum, acc[d]) partial per query head, then
-// merges its slice of the pair's output from all the pair's partials; the
-// last to finish clears the pair's headers and candidates and advances its
-// epoch.
+// Hand-offs are 64-bit words read with device-scope loads: headers and
+// candidates are never 0 once written (cleared after use); weights and
+// partials carry the call's epoch in their upper half.  Readers poll such
+// words directly, so publishing needs no completion wait.  When the device
+// sends workgroups to its XCDs round robin, all workgroups of a pair run on
+// one XCD and the words are stored with the default policy, so they are
+// handed over in that XCD's L2; otherwise they are written through.
 //
 // The grid covers bg_round pairs at once and walks the rest in rounds; the
 // host launches it only when the whole grid can be resident, so the
@@ -173,9 +177,11 @@ __device__ __forceinline__ float read_tagged(const Coh& src, int i, uint64_t v, 
 // Per-thread attention state of G query heads -> one partial per head at
 // `part` ([G][D + 2] tagged words: max, sum, acc[D]), combining the row
 // slots of each wave with lane swaps, then the waves through LDS.
+// With `extra`, the partial published there by another workgroup (same
+// layout and tag) is folded in first.
 template <int D, int G>
 __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8], float (*red)[G][D + 4],
-                                const Coh& part, uint32_t tag) {
+                                const Coh& part, uint32_t tag, const Coh* extra, uint32_t* err) {
   constexpr int LPR = D / 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = tid % LPR;
 #pragma unroll
@@ -220,6 +226,20 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
       Ls = fmaf(rw[1], f, Ls);
     }
     const int h = j * (D + 2);
+    if (extra) {
+      uint32_t spins = 0;
+      const uint64_t w0 = extra->u64(h), w1 = extra->u64(h + 1), w2 = extra->u64(h + 2 + 2 * d2),
+                     w3 = extra->u64(h + 3 + 2 * d2);
+      const float me = read_tagged(*extra, h, w0, tag, spins, err);
+      const float le = read_tagged(*extra, h + 1, w1, tag, spins, err);
+      const float e0 = read_tagged(*extra, h + 2 + 2 * d2, w2, tag, spins, err);
+      const float e1 = read_tagged(*extra, h + 3 + 2 * d2, w3, tag, spins, err);
+      const float M = fmaxf(Mx, me), f1 = scale_from(Mx, M), f2 = scale_from(me, M);
+      a0 = a0 * f1 + e0 * f2;
+      a1 = a1 * f1 + e1 * f2;
+      Ls = Ls * f1 + le * f2;
+      Mx = M;
+    }
     part.put_u64(h + 2 + 2 * d2, tagged(a0, tag));
     part.put_u64(h + 3 + 2 * d2, tagged(a1, tag));
     if (d2 == 0) {
@@ -685,7 +705,11 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + chunk) * G * (D + 2), (size_t)G * (D + 2) * 8,
                  s.n_xcd > 0);
-  publish_partial<D, G>(m, l, acc, L.u.red, part, tag);
+  // the value workgroup of this chunk publishes its compensation sums first;
+  // they are folded into this partial, so the merge reads one per chunk
+  const Coh vpart(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
+                  (size_t)G * (D + 2) * 8, s.n_xcd > 0);
+  publish_partial<D, G>(m, l, acc, L.u.red, part, tag, &vpart, err);
 
   // ---- the selection outputs ----
   if (chunk == 0) {
@@ -769,12 +793,13 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
                  (size_t)G * (D + 2) * 8, s.n_xcd > 0);
-  publish_partial<D, G>(m, l, acc, L.red, part, tag);
+  publish_partial<D, G>(m, l, acc, L.red, part, tag, nullptr, err);
 }
 
 // ---------------------------------------------------------------------------
 // Workgroup `slot` (of the pair's 2 * n_chunks) merges its slice of the
-// pair's output from all the pair's partials, waiting for each to carry this
+// pair's output from the partials of the pair's control workgroups (each
+// holding its chunk's compensation sums too), waiting for each to carry this
 // call's tag.  The last workgroup to finish resets the pair for the next call.
 // ---------------------------------------------------------------------------
 template <int D, int G>
@@ -786,11 +811,12 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t tag = epoch + 1u;
   uint32_t* err = w.ctrl + 2;
-  const int np = 2 * s.n_chunks;
-  const int per = (NV + np - 1) / np;  // float4 outputs of this workgroup
+  const int nm = 2 * s.n_chunks;      // merging workgroups of the pair
+  const int np = s.n_chunks;          // partials: one per chunk (value sums folded in)
+  const int per = (NV + nm - 1) / nm;  // float4 outputs of this workgroup
   const int step = max(1, NT / np);    // outputs merged per pass
   const int o0 = slot * per, o1 = min(NV, o0 + per);
-  const Coh part(w.fpart + (size_t)bg * np * G * (D + 2), (size_t)np * G * (D + 2) * 8, s.n_xcd > 0);
+  const Coh part(w.fpart + (size_t)bg * nm * G * (D + 2), (size_t)np * G * (D + 2) * 8, s.n_xcd > 0);
   uint32_t spins = 0;
   for (int base = o0; base < o1; base += step) {
     // the (output, partial) items of this pass: six words each, read together
@@ -849,7 +875,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
     __syncthreads();
   }
   // the last workgroup of the pair to finish resets it for the next call
-  if (arrive(ctr_done(w, bg), sh) != (uint32_t)(np - 1)) return;
+  if (arrive(ctr_done(w, bg), sh) != (uint32_t)(nm - 1)) return;
   const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
   const int M = (Lseq + s.bs - 1) / s.bs;
   const int kk = min(M, s.kmax);
