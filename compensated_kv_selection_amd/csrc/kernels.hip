@@ -64,46 +64,58 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
   const int n = min(s.bs, L - i * s.bs);
   const float fn = (float)n;
 
-  for (int item = threadIdx.x; item < s.Hkv * LPR; item += blockDim.x) {
-    const int g = item / LPR, c = item % LPR;
-    const size_t tile = ((size_t)page * s.Hkv + g) * s.bs * D + c * 8;
-    const KV* kp = kc + tile;
-    const KV* vp = vc + tile;
-    // Means on data shifted by the first token: a block of equal tokens gets
-    // exactly that token as mean and zero variance.
-    float k0[8], v0[8], sk[8], sv[8], x[8];
-    load8(kp, k0);
-    load8(vp, v0);
+  // One item per (K or V, KV head, 8-channel slice): the first Hkv * LPR
+  // items take the keys, the rest the values.  All 16 rows of the page are
+  // requested at once (rows past the sequence lie in the page and are not
+  // used).  Means on data shifted by the first token: a block of equal tokens
+  // gets exactly that token as mean and zero variance.
+  static_assert(kBlockSize == 16, "one page holds 16 tokens");
+  const int nk = s.Hkv * LPR;
+  for (int item = threadIdx.x; item < 2 * nk; item += blockDim.x) {
+    const bool isv = item >= nk;
+    const int it = isv ? item - nk : item;
+    const int g = it / LPR, c = it % LPR;
+    const KV* p = (isv ? vc : kc) + ((size_t)page * s.Hkv + g) * s.bs * D + c * 8;
+    Raw8<KV> raw[kBlockSize];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { sk[e] = 0.f; sv[e] = 0.f; }
-    for (int t = 1; t < n; ++t) {
-      load8(kp + t * D, x);
+    for (int t = 0; t < kBlockSize; ++t) raw_load(p + t * D, raw[t]);
+    float x0[8], sx[8], x[8];
+    raw_float(raw[0], x0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sk[e] += x[e] - k0[e];
-      load8(vp + t * D, x);
+    for (int e = 0; e < 8; ++e) sx[e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] += x[e] - v0[e];
-    }
-    float mu[8], nu[8], var[8];
+    for (int t = 1; t < kBlockSize; ++t) {
+      if (t < n) {
+        raw_float(raw[t], x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mu[e] = k0[e] + sk[e] / fn;
-      nu[e] = v0[e] + sv[e] / fn;
-      var[e] = 0.f;
-    }
-    for (int t = 0; t < n; ++t) {  // second pass: population variance
-      load8(kp + t * D, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float dl = x[e] - mu[e];
-        var[e] = fmaf(dl, dl, var[e]);
+        for (int e = 0; e < 8; ++e) sx[e] += x[e] - x0[e];
       }
     }
+    float mu[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) var_sh[g * D + c * 8 + e] = var[e] / fn;
+    for (int e = 0; e < 8; ++e) mu[e] = x0[e] + sx[e] / fn;
     const size_t row = (((size_t)b * s.Hkv + g) * s.max_blocks + i) * D + c * 8;
-    store8(mk + row, mu);
-    store8(mv + row, nu);
+    if (isv) {
+      store8(mv + row, mu);
+    } else {
+      float var[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) var[e] = 0.f;
+#pragma unroll
+      for (int t = 0; t < kBlockSize; ++t) {  // second pass: population variance
+        if (t < n) {
+          raw_float(raw[t], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float dl = x[e] - mu[e];
+            var[e] = fmaf(dl, dl, var[e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) var_sh[g * D + c * 8 + e] = var[e] / fn;
+      store8(mk + row, mu);
+    }
   }
   __syncthreads();
   const int gs = D / s.r;
