@@ -71,6 +71,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
   // gets exactly that token as mean and zero variance.
   static_assert(kBlockSize == 16, "one page holds 16 tokens");
   const int nk = s.Hkv * LPR;
+  const int gs = D / s.r;                     // channels per group
+  const bool lanes_sum = gs % 8 == 0;         // a group is whole 8-channel slices of adjacent lanes
   for (int item = threadIdx.x; item < 2 * nk; item += blockDim.x) {
     const bool isv = item >= nk;
     const int it = isv ? item - nk : item;
@@ -95,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) mu[e] = x0[e] + sx[e] / fn;
     const size_t row = (((size_t)b * s.Hkv + g) * s.max_blocks + i) * D + c * 8;
+    float vs = 0.f;  // keys: the slice's channel variances summed
     if (isv) {
       store8(mv + row, mu);
     } else {
@@ -112,18 +115,36 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
           }
         }
       }
+      if (lanes_sum) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) var_sh[g * D + c * 8 + e] = var[e] / fn;
+        for (int e = 0; e < 8; ++e) vs += var[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) var_sh[g * D + c * 8 + e] = var[e] / fn;
+      }
       store8(mk + row, mu);
     }
+    if (lanes_sum) {
+      // the group's slices are adjacent lanes of one row (gs / 8 of them,
+      // aligned): sum them across lanes
+      const int wl = gs / 8;
+      float gsum = vs;
+      if (wl > 1) gsum += __uint_as_float(lane_xor<1>(__float_as_uint(gsum)));
+      if (wl > 2) gsum += __uint_as_float(lane_xor<2>(__float_as_uint(gsum)));
+      if (wl > 4) gsum += __uint_as_float(lane_xor<4>(__float_as_uint(gsum)));
+      if (wl > 8) gsum += __uint_as_float(lane_xor<8>(__float_as_uint(gsum)));
+      if (!isv && c % wl == 0)
+        gv[(((size_t)b * s.Hkv + g) * s.max_blocks + i) * s.r + c / wl] = gsum / (fn * (float)gs);
+    }
   }
-  __syncthreads();
-  const int gs = D / s.r;
-  for (int item = threadIdx.x; item < s.Hkv * s.r; item += blockDim.x) {
-    const int g = item / s.r, t = item % s.r;
-    float acc = 0.f;
-    for (int c = 0; c < gs; ++c) acc += var_sh[g * D + t * gs + c];
-    gv[(((size_t)b * s.Hkv + g) * s.max_blocks + i) * s.r + t] = acc / (float)gs;
+  if (!lanes_sum) {
+    __syncthreads();
+    for (int item = threadIdx.x; item < s.Hkv * s.r; item += blockDim.x) {
+      const int g = item / s.r, t = item % s.r;
+      float acc = 0.f;
+      for (int c = 0; c < gs; ++c) acc += var_sh[g * D + t * gs + c];
+      gv[(((size_t)b * s.Hkv + g) * s.max_blocks + i) * s.r + t] = acc / (float)gs;
+    }
   }
   if (threadIdx.x == 0) cnt[(size_t)b * s.max_blocks + i] = n;
 }
