@@ -93,6 +93,87 @@ def rocprof_summary(directory: str) -> str:
     return "\n".join(lines) if lines else f"no rocprofv3 CSV files under {directory}"
 
 
+def graph_time_us(torch, fn, n: int) -> float:
+    """Mean time of fn(i), i = 0..n-1, captured in one HIP graph and replayed
+    (events on the current stream around the timed replay)."""
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def sweep(args, dev0) -> int:
+    """Step latency over context lengths and budgets: 32K, 64K, 128K tokens x
+    512, 1024, 2048-token budgets (the CompKV review's length/budget grid is
+    not printed; this is its plainest reading), Llama-3.1-8B layer shape,
+    synthetic inputs.  Steps rotate over enough layer copies that their
+    summaries exceed the last-level cache."""
+    import torch
+    from compensated_kv_selection_amd import compkv as C
+    from compensated_kv_selection_amd import workloads as W
+    from compensated_kv_selection_amd.tensors import to_device
+    for L in (32768, 65536, 131072):
+        w = W.make_decode_inputs(name=f"sweep_{L}", seq_lens=[L], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                 block_size=16, r_groups=4, budget_tokens=512, dtype="bf16", n_needles=16,
+                                 n_outliers=4, seed=args.seed)
+        base = to_device(w, dev0)
+        dims = base.dims
+        M = -(-L // 16)
+        summary_bytes = M * 8 * (2 * 128 * 2 + 4 * 4) + 4 * M
+        n_layers = max(2, -(-(512 << 20) // summary_bytes))
+        layers = []
+        for li in range(n_layers):
+            kc = base.k_cache if li == 0 else base.k_cache.clone()
+            vc = base.v_cache if li == 0 else base.v_cache.clone()
+            summ = C.allocate_summaries(dims, dev0)
+            C.build_summaries(dims, kc, vc, base.block_table, base.seq_lens, summ)
+            layers.append((kc, vc, summ))
+        torch.cuda.synchronize()
+        out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev0)
+        lse = torch.empty((1, 32), dtype=torch.float32, device=dev0)
+        dws = C.allocate_workspace(C.dense_workspace_bytes(dims), dev0)
+
+        def dstep(i):
+            kc, vc, _ = layers[i % n_layers]
+            C.dense_decode_attention(dims, base.q, kc, vc, base.block_table, base.seq_lens, dws, out=out, lse=lse)
+
+        dense_us = graph_time_us(torch, dstep, 32)
+        for budget in (512, 1024, 2048):
+            ws = C.allocate_workspace(C.workspace_bytes(dims, budget), dev0)
+            kk = min(M, budget // 16)
+            sel = torch.empty((1, 8, max(1, kk)), dtype=torch.int32, device=dev0)
+            nsel = torch.empty((1, 8), dtype=torch.int32, device=dev0)
+
+            def step(i):
+                kc, vc, summ = layers[i % n_layers]
+                C.decode_step(dims, base.q, kc, vc, summ, base.block_table, base.seq_lens, budget, ws,
+                              selected=sel, num_selected=nsel, out=out, lse=lse)
+
+            us = graph_time_us(torch, step, 100)
+            ab = algorithmic_bytes(M, 8, 128, 4, kk, 16, 2)
+            gbps = ab["total"] / (us * 1e-6) / 1e9
+            print(json.dumps({"sweep": "decode step latency", "seq_len": L, "budget_tokens": budget,
+                              "us_per_step": round(us, 2), "launches": C.decode_step_launches(dims, budget),
+                              "algorithmic_bytes": ab["total"], "effective_GBps": round(gbps, 1),
+                              "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+                              "dense_us": round(dense_us, 2), "speedup_vs_dense": round(dense_us / us, 2),
+                              "layer_copies": n_layers, "data": "synthetic"}), flush=True)
+        del layers
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +189,9 @@ def main() -> int:
                     help="only run a plain elementwise copy of this many MiB (counter calibration)")
     ap.add_argument("--rocprof-summary", default="",
                     help="only print a per-kernel summary of the rocprofv3 CSV files under this directory")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the step over context lengths 32K, 64K, 128K x budgets 512, 1024, 2048 "
+                         "tokens (Llama-3.1-8B layer shape), with dense decode per length; one JSON line each")
     args = ap.parse_args()
 
     if args.rocprof_summary:
@@ -146,6 +230,8 @@ def main() -> int:
         return 0
 
     C.load_library()
+    if args.sweep:
+        return sweep(args, dev0)
     t_gen = time.time()
     w = W.make_preset(args.workload, seed=args.seed)
     print(f"[bench] generated {args.workload} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
