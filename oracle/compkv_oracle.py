@@ -457,3 +457,107 @@ def kl_divergence(p_hat: np.ndarray, p: np.ndarray) -> float:
     """KL(p_hat || p) = sum p_hat log(p_hat / p) over the support of p_hat."""
     m = p_hat > 0
     return float((p_hat[m] * (np.log(p_hat[m]) - np.log(p[m]))).sum())
+
+
+# ---------------------------------------------------------------------------
+# Selection fidelity ([review Strengths]: App. B.1 compares ranking blocks by
+# the exact residual with ranking them by attention mass, through the KL
+# divergence to exact attention and the relative L2 error of the output;
+# App. B.2 measures how well the practical score tracks the exact residual,
+# by rank correlation and by the share of the best attainable residual that
+# its selection keeps)
+# ---------------------------------------------------------------------------
+
+
+def token_distribution(q: np.ndarray, k: np.ndarray, summ: Summaries, selected: np.ndarray,
+                       block_size: int, h: int, compensate: bool = True) -> np.ndarray:
+    """Attention distribution of query head h over all L tokens under a
+    selection: a token of a selected block keeps its weight exp(s_j); every
+    token of an omitted block gets its block's mean-key weight exp(s_bar)
+    (Mean compensation) or weight zero (no compensation).  Normalised."""
+    Hq, d = q.shape
+    L, Hkv, _ = k.shape
+    g = h // (Hq // Hkv)
+    tau = 1.0 / math.sqrt(d)
+    logit = tau * (k[:, g, :] @ q[h])
+    blk = np.arange(L) // block_size
+    chosen = np.zeros(summ.num_blocks, dtype=bool)
+    chosen[np.asarray(selected[g], dtype=np.int64)] = True
+    if compensate:
+        s_bar = tau * (summ.mean_k[:, g, :] @ q[h])
+        logit = np.where(chosen[blk], logit, s_bar[blk])
+    else:
+        logit = np.where(chosen[blk], logit, -np.inf)
+    if not np.isfinite(logit).any():
+        return np.zeros(L)
+    w = np.exp(logit - logit.max())
+    return w / w.sum()
+
+
+def dense_distribution(q: np.ndarray, k: np.ndarray, h: int) -> np.ndarray:
+    """Softmax of query head h's exact logits over all tokens."""
+    Hq, d = q.shape
+    g = h // (Hq // k.shape[1])
+    s = (k[:, g, :] @ q[h]) / math.sqrt(d)
+    w = np.exp(s - s.max())
+    return w / w.sum()
+
+
+@dataclasses.dataclass
+class Fidelity:
+    kl: np.ndarray       # [Hq] KL(p_hat || p) against exact attention
+    rel_l2: np.ndarray   # [Hq] ||out - out_dense||_2 / ||out_dense||_2
+
+
+def selection_fidelity(q: np.ndarray, k: np.ndarray, v: np.ndarray, summ: Summaries,
+                       selected: np.ndarray, block_size: int, compensate: bool = True,
+                       dense=None) -> Fidelity:
+    """How far one selection (with or without Mean compensation) lands from
+    exact attention, per query head.  ``dense`` may pass in a previous
+    ``dense_attention`` result."""
+    Hq = q.shape[0]
+    out, _ = compensated_attention(q, k, v, summ, selected, block_size, compensate)
+    d_out, _ = dense if dense is not None else dense_attention(q, k, v)
+    kl = np.array([kl_divergence(token_distribution(q, k, summ, selected, block_size, h, compensate),
+                                 dense_distribution(q, k, h)) for h in range(Hq)])
+    rel = np.linalg.norm(out - d_out, axis=1) / np.linalg.norm(d_out, axis=1)
+    return Fidelity(kl, rel)
+
+
+def average_ranks(x: np.ndarray) -> np.ndarray:
+    """Ranks 1..n in ascending order of x; equal values share the mean of the
+    ranks they span."""
+    x = np.asarray(x, dtype=np.float64)
+    order = np.argsort(x, kind="stable")
+    xs = x[order]
+    ranks = np.empty(x.size)
+    i = 0
+    while i < x.size:
+        j = i
+        while j + 1 < x.size and xs[j + 1] == xs[i]:
+            j += 1
+        ranks[order[i:j + 1]] = 0.5 * (i + j) + 1.0
+        i = j + 1
+    return ranks
+
+
+def spearman(a: np.ndarray, b: np.ndarray) -> float:
+    """Spearman rank correlation: the Pearson correlation of the two
+    samples' average ranks."""
+    ra, rb = average_ranks(a), average_ranks(b)
+    ra -= ra.mean()
+    rb -= rb.mean()
+    return float((ra * rb).sum() / math.sqrt((ra * ra).sum() * (rb * rb).sum()))
+
+
+def residual_capture(resid: np.ndarray, selected: np.ndarray) -> np.ndarray:
+    """Per KV head: the exact residual the selection keeps, as a share of the
+    most any selection of the same size can keep (the top-k by the exact
+    residual).  ``resid`` is [Hkv, M], e.g. the group sum of resid / Z."""
+    Hkv = resid.shape[0]
+    out = np.zeros(Hkv)
+    for g in range(Hkv):
+        sel = np.asarray(selected[g], dtype=np.int64)
+        best = np.sort(resid[g])[::-1][:sel.size].sum()
+        out[g] = resid[g, sel].sum() / best if best > 0 else 1.0
+    return out
