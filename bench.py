@@ -16,6 +16,7 @@ same GPU, and the CPU oracle timed on the host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -174,6 +175,74 @@ def sweep(args, dev0) -> int:
     return 0
 
 
+def decode_loop(args, dev0) -> int:
+    """Prefill plus a generation loop at 128K context (Llama-3.1-8B layer
+    shape): the bulk summary build over 131072 tokens, then 64 decode steps,
+    each appending one token (written into its page and the tail block's
+    summary refreshed, in one launch) and running the step with a 2048-token
+    budget.  The
+    steps of all layer copies are captured into one HIP graph and replayed;
+    a step visits every layer copy in turn, as a model's layer loop would, so
+    summaries come from HBM."""
+    import numpy as np
+    import torch
+    from compensated_kv_selection_amd import compkv as C
+    from compensated_kv_selection_amd import workloads as W
+    from compensated_kv_selection_amd.decode_loop import DecodeLoop
+    from compensated_kv_selection_amd.tensors import to_device
+
+    n_steps = 64
+    w = W.make_preset("prefill_128k_loop", seed=args.seed)
+    steps = W.make_append_steps(w, n_steps, seed=args.seed + 1)
+    kc, vc = w.paged_cache()
+    base = to_device(w, dev0, k_cache=kc, v_cache=vc)
+    del kc, vc
+    dims = base.dims
+    n_layers = max(1, args.loop_layers)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    loops, build_ms = [], []
+    for li in range(n_layers):
+        dev = base if li == 0 else dataclasses.replace(
+            base, k_cache=base.k_cache.clone(), v_cache=base.v_cache.clone(), q=base.q.clone(),
+            seq_lens=base.seq_lens.clone())
+        summ = C.allocate_summaries(dims, dev0)
+        torch.cuda.synchronize()
+        ev[0].record()
+        C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
+        ev[1].record()
+        torch.cuda.synchronize()
+        build_ms.append(ev[0].elapsed_time(ev[1]))
+        loops.append(DecodeLoop(dev, summ, w.block_table, w.seq_lens, steps, w.dtype))
+
+    def run_all():
+        for t in range(n_steps):
+            for lp in loops:
+                lp.step(t)
+
+    run_all()  # eager pass
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    ev[0].record()
+    g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / (n_steps * n_layers)
+    print(json.dumps({"decode_loop": "prefill + 64 appending decode steps, graph replay",
+                      "seq_len_start": int(w.seq_lens[0]), "steps": n_steps,
+                      "budget_tokens": w.budget_tokens, "layer_copies": n_layers,
+                      "prefill_build_us": round(float(np.median(build_ms)) * 1e3, 1),
+                      "us_per_layer_step": round(us, 2),
+                      "per_layer_step": "length and query copies, ckv_append_tokens (new key and value "
+                                        "into their page, tail-block summary), ckv_decode_step",
+                      "launches_per_decode_step": C.decode_step_launches(dims, w.budget_tokens),
+                      "data": "synthetic"}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +261,10 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="only time the step over context lengths 32K, 64K, 128K x budgets 512, 1024, 2048 "
                          "tokens (Llama-3.1-8B layer shape), with dense decode per length; one JSON line each")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="only time the prefill summary build and a 64-step appending decode loop at 128K "
+                         "context, 2048-token budget, captured into one HIP graph; one JSON line")
+    ap.add_argument("--loop-layers", type=int, default=8, help="layer copies the decode loop visits per step")
     args = ap.parse_args()
 
     if args.rocprof_summary:
@@ -232,6 +305,8 @@ def main() -> int:
     C.load_library()
     if args.sweep:
         return sweep(args, dev0)
+    if args.decode_loop:
+        return decode_loop(args, dev0)
     t_gen = time.time()
     w = W.make_preset(args.workload, seed=args.seed)
     print(f"[bench] generated {args.workload} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)

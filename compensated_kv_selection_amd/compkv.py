@@ -24,6 +24,7 @@ SCORE_COMPKV, SCORE_MASS = 0, 1
 # Every symbol include/compkv.h declares.
 EXPORTS = (
     "ckv_build_summaries",
+    "ckv_append_tokens",
     "ckv_workspace_bytes",
     "ckv_score_select",
     "ckv_compensated_decode_attention",
@@ -71,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     S = ctypes.POINTER(CkvSummaries)
     sig = {
         "ckv_build_summaries": (I32, [D, P, P, P, P, I32, S, P]),
+        "ckv_append_tokens": (I32, [D, P, P, P, P, P, P, S, P]),
         "ckv_workspace_bytes": (SZ, [D, I32]),
         "ckv_score_select": (I32, [D, P, S, P, P, I32, I32, P, P, P, P, SZ, P]),
         "ckv_compensated_decode_attention": (I32, [D, P, P, P, S, P, P, I32, P, P, I32, P, P, P, SZ, P]),
@@ -161,6 +163,18 @@ def build_summaries(dims: Dims, k_cache, v_cache, block_table, seq_lens, summari
     _check(lib.ckv_build_summaries(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                    _ptr(seq_lens), 1 if append_only else 0, ctypes.byref(s),
                                    _stream(k_cache.device)))
+
+
+def append_tokens(dims: Dims, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                  summaries: Summaries) -> None:
+    """Write every sequence's new last token (k_new, v_new: [B, Hkv, d]) into
+    its page and refresh that block's summary, in one launch; seq_lens
+    already count the new token."""
+    lib = load_library()
+    d = dims.c()
+    s = summaries.c()
+    _check(lib.ckv_append_tokens(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_table), _ptr(seq_lens), ctypes.byref(s), _stream(k_cache.device)))
 
 
 def workspace_bytes(dims: Dims, budget_tokens: int) -> int:

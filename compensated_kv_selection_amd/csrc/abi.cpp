@@ -1,5 +1,6 @@
 // C ABI of libcompkv.so: host-side argument checks, workspace carving and
 // launch order.  Every check runs before anything is enqueued.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -76,6 +77,7 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.share = x.kmax > 0 ? (x.kmax + x.n_chunks - 1) / x.n_chunks : 1;
   x.bg_round = 0;
   x.n_xcd = 0;
+  x.n_val = x.n_chunks;
   int splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
   splits = splits < 1 ? 1 : (splits > ckv::kMaxSplits ? ckv::kMaxSplits : splits);
   x.n_splits = splits;
@@ -179,30 +181,51 @@ ckv::Summ to_summ(const ckv_summaries* sm) {
   return ckv::Summ{sm->mean_k, sm->mean_v, sm->gvar, sm->count};
 }
 
-// One launch when its whole grid - at least the two workgroups of every chunk
-// of one (sequence, KV head) pair - can be resident at once, the pair's
-// candidates fit in shared memory and page ids fit in its selection keys;
-// otherwise three launches that never wait.
-// Sets s->bg_round (pairs per round of the persistent grid) when fused.
-// When blocks go to the device's XCDs round robin (checked once per device,
-// not while `stream` is capturing) and the workgroups of one pair fit on one
-// XCD at once, every pair is kept on one XCD (s->n_xcd set), so that its
+// Value workgroups per pair and pairs per round when `pairs` pairs share
+// `cap` resident workgroups: the fewest rounds, then the most value
+// workgroups (one per chunk, down to one per two chunks).  rounds == 0: not
+// even one pair fits.
+struct Fit {
+  int n_val = 0, per_round = 0, rounds = 0;
+};
+Fit fit_pairs(int n_chunks, int cap, int pairs) {
+  Fit best;
+  for (int nv = n_chunks; nv >= (n_chunks + 1) / 2; --nv) {
+    const int per = std::min(pairs, cap / (n_chunks + nv));
+    if (per < 1) continue;
+    const int rounds = (pairs + per - 1) / per;
+    if (best.rounds == 0 || rounds < best.rounds) best = Fit{nv, per, rounds};
+  }
+  return best;
+}
+
+// One launch when its whole grid - at least the control workgroups of every
+// chunk of one (sequence, KV head) pair and a value workgroup per two chunks -
+// can be resident at once, the pair's candidates fit in shared memory and page
+// ids fit in its selection keys; otherwise three launches that never wait.
+// Sets s->bg_round (pairs per round of the persistent grid) and s->n_val when
+// fused.  When blocks go to the device's XCDs round robin (checked once per
+// device, not while `stream` is capturing) and keeping every pair on one XCD
+// takes no more rounds, each pair stays on one XCD (s->n_xcd set), so that its
 // workgroups hand data to each other through that XCD's L2.
 bool plan_fused(ckv::Shape* s, hipStream_t stream, bool probe) {
-  const int resident = ckv::fused_resident_workgroups(*s);
-  const int per_round = resident / (2 * s->n_chunks);
-  if (per_round < 1 || s->share > ckv::kShareMax || s->n_chunks * s->kmax > ckv::kFusedCand) return false;
+  if (s->share > ckv::kShareMax || s->n_chunks * s->kmax > ckv::kFusedCand) return false;
   if (s->P >= (1 << ckv::kFusedPageBits)) return false;
+  const int resident = ckv::fused_resident_workgroups(*s);
   const int bgs = s->B * s->Hkv;
-  s->bg_round = per_round < bgs ? per_round : bgs;
+  const Fit spread = fit_pairs(s->n_chunks, resident, bgs);
+  if (spread.rounds == 0) return false;
+  s->n_val = spread.n_val;
+  s->bg_round = spread.per_round;
   s->n_xcd = 0;
   const char* off = getenv("CKV_FUSED_ACROSS_XCDS");
   const int nx = probe && !(off && off[0] == '1') ? ckv::fused_xcd_count(stream) : 0;
   if (nx > 0) {
-    const int per_xcd = resident / nx / (2 * s->n_chunks);  // pairs one XCD holds at once
-    if (per_xcd >= 1) {
+    const Fit local = fit_pairs(s->n_chunks, resident / nx, (bgs + nx - 1) / nx);  // per XCD
+    if (local.rounds > 0 && local.rounds <= spread.rounds) {
       s->n_xcd = nx;
-      s->bg_round = nx * per_xcd < bgs ? nx * per_xcd : bgs;
+      s->n_val = local.n_val;
+      s->bg_round = std::min(bgs, nx * local.per_round);
     }
   }
   return true;
@@ -238,6 +261,20 @@ ckv_status ckv_build_summaries(const ckv_dims* dims, const void* k_cache, const 
                                                 append_only ? 1 : 0, to_summ(summaries),
                                                 static_cast<hipStream_t>(stream)),
                     "summary build launch");
+}
+
+ckv_status ckv_append_tokens(const ckv_dims* dims, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const ckv_summaries* summaries, void* stream) {
+  ckv::Shape s;
+  CKV_TRY(make_shape(dims, 0, &s));
+  if (!k_new || !v_new) return fail(CKV_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  if (!k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "k_cache or v_cache is NULL");
+  if (!block_table || !seq_lens) return fail(CKV_ERR_INVALID_ARG, "block_table or seq_lens is NULL");
+  CKV_TRY(check_summaries(summaries));
+  return hip_status(ckv::launch_append_tokens(s, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                              to_summ(summaries), static_cast<hipStream_t>(stream)),
+                    "append launch");
 }
 
 size_t ckv_workspace_bytes(const ckv_dims* dims, int32_t budget_tokens) {

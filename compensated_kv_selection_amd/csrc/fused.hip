@@ -13,7 +13,10 @@
 // n e^{s_bar} and value mean_v.
 //
 // Organisation.  Every (sequence, KV head) pair is split into chunks of 256
-// blocks, and every chunk gets two workgroups of 4 waves:
+// blocks.  Every chunk gets a control workgroup of 4 waves, and the pair gets
+// n_val value workgroups of 4 waves: one per chunk when the whole grid fits on
+// the device at once, else as few as make it fit (down to one per two
+// chunks), value workgroup v taking chunks v, v + n_val, ... in turn:
 //   a control workgroup loads the chunk's mean keys, grouped variances and
 //     page-table entries, computes the block-mean logits on the matrix cores
 //     (the G query heads are the rows of a 16x16x32 bf16 MFMA tile),
@@ -23,10 +26,11 @@
 //     candidate of the pair, finds the pair's top-k, attends exactly to its
 //     share of the selected blocks (ranks chunk, chunk + n_chunks, ... of the
 //     pair's selection), takes back the compensation terms of the selected
-//     blocks of its chunk, folds in the value workgroup's sums and publishes
+//     blocks of its chunk, folds in the chunk's value sums and publishes
 //     one (max, sum, acc[d]) partial per query head;
-//   a value workgroup waits for the chunk's weights, streams the chunk's mean
-//     values and sums the compensation terms of all the chunk's blocks.
+//   a value workgroup waits for a chunk's weights, streams the chunk's mean
+//     values, sums the compensation terms of all the chunk's blocks and
+//     publishes them for the chunk's control workgroup.
 // Then every workgroup of the pair merges its slice of the pair's output from
 // the control workgroups' partials; the last to finish clears the pair's
 // headers and candidates and advances its epoch.
@@ -797,7 +801,7 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup `slot` (of the pair's 2 * n_chunks) merges its slice of the
+// Workgroup `slot` (of the pair's n_chunks + n_val) merges its slice of the
 // pair's output from the partials of the pair's control workgroups (each
 // holding its chunk's compensation sums too), waiting for each to carry this
 // call's tag.  The last workgroup to finish resets the pair for the next call.
@@ -811,12 +815,13 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t tag = epoch + 1u;
   uint32_t* err = w.ctrl + 2;
-  const int nm = 2 * s.n_chunks;      // merging workgroups of the pair
-  const int np = s.n_chunks;          // partials: one per chunk (value sums folded in)
+  const int nm = s.n_chunks + s.n_val;  // merging workgroups of the pair
+  const int np = s.n_chunks;            // partials: one per chunk (value sums folded in)
   const int per = (NV + nm - 1) / nm;  // float4 outputs of this workgroup
   const int step = max(1, NT / np);    // outputs merged per pass
   const int o0 = slot * per, o1 = min(NV, o0 + per);
-  const Coh part(w.fpart + (size_t)bg * nm * G * (D + 2), (size_t)np * G * (D + 2) * 8, s.n_xcd > 0);
+  const Coh part(w.fpart + (size_t)bg * 2 * s.n_chunks * G * (D + 2), (size_t)np * G * (D + 2) * 8,
+                 s.n_xcd > 0);
   uint32_t spins = 0;
   for (int base = o0; base < o1; base += step) {
     // the (output, partial) items of this pass: six words each, read together
@@ -911,30 +916,42 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
   __shared__ FusedLds<D, G> lds;
   __shared__ uint32_t sh[4];
   warm_kernel_args();
-  // This workgroup's pair (of the round), role and chunk.  Kept on one XCD
-  // (n_xcd > 0): workgroup i runs on XCD i % n_xcd, which takes the pairs
-  // p = XCD, XCD + n_xcd, ...; otherwise control workgroups come first.
+  // This workgroup's pair (of the round) and role: control workgroup of
+  // chunk `role` (role < n_chunks), else value workgroup role - n_chunks.
+  // Kept on one XCD (n_xcd > 0): workgroup i runs on XCD i % n_xcd, which
+  // takes the pairs p = XCD, XCD + n_xcd, ...; otherwise control workgroups
+  // come first.
+  const int wpp = s.n_chunks + s.n_val;  // workgroups per pair
   int pair, role;
   if (s.n_xcd > 0) {
     const int slot = (int)blockIdx.x / s.n_xcd;
-    pair = (int)blockIdx.x % s.n_xcd + s.n_xcd * (slot / (2 * s.n_chunks));
-    role = slot % (2 * s.n_chunks);
+    pair = (int)blockIdx.x % s.n_xcd + s.n_xcd * (slot / wpp);
+    role = slot % wpp;
     if (pair >= s.bg_round) return;
   } else {
     const int half = s.bg_round * s.n_chunks;
-    const bool c = (int)blockIdx.x < half;
-    const int t = c ? (int)blockIdx.x : (int)blockIdx.x - half;
-    pair = t / s.n_chunks;
-    role = (c ? 0 : s.n_chunks) + t % s.n_chunks;
+    if ((int)blockIdx.x < half) {
+      pair = (int)blockIdx.x / s.n_chunks;
+      role = (int)blockIdx.x % s.n_chunks;
+    } else {
+      const int t = (int)blockIdx.x - half;
+      pair = t / s.n_val;
+      role = s.n_chunks + t % s.n_val;
+    }
   }
-  const bool ctl = role < s.n_chunks;
-  const int chunk = role % s.n_chunks;
   for (int bg = pair; bg < s.B * s.Hkv; bg += s.bg_round) {
     const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
-    if (ctl) ctl_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.c);
-    else val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
+    if (role < s.n_chunks) {
+      ctl_chunk<KV, D, G>(s, io, w, bg, role, epoch + 1u, lds.c);
+    } else {
+      // value workgroup v sums chunks v, v + n_val, ... in turn
+      for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
+        val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
+        __syncthreads();
+      }
+    }
     __syncthreads();
-    merge_slice<D, G>(s, io, w, bg, ctl ? chunk : s.n_chunks + chunk, epoch, lds.m, sh);
+    merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m, sh);
     __syncthreads();
   }
 }
@@ -1014,8 +1031,8 @@ int fused_xcd_count(hipStream_t st) {
 }
 
 hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t st) {
-  const dim3 grid(s.n_xcd > 0 ? s.n_xcd * ((s.bg_round + s.n_xcd - 1) / s.n_xcd) * 2 * s.n_chunks
-                              : 2 * s.bg_round * s.n_chunks);
+  const int wpp = s.n_chunks + s.n_val;
+  const dim3 grid(s.n_xcd > 0 ? s.n_xcd * ((s.bg_round + s.n_xcd - 1) / s.n_xcd) * wpp : s.bg_round * wpp);
   return with_fused(s, [&](auto fn, int) {
     hipLaunchKernelGGL(fn, grid, dim3(NT), 0, st, s, io, w);
     return hipGetLastError();

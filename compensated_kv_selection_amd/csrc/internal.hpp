@@ -46,6 +46,8 @@ struct Shape {
   int share;          // selected blocks attended by one chunk workgroup (fused)
   int bg_round;       // (sequence, KV head) pairs processed at once by the fused grid
   int n_xcd;          // fused: > 0 = XCDs of the device, each pair kept on one XCD; 0 = spread
+  int n_val;          // fused: value workgroups per pair, 1..n_chunks; value workgroup v sums
+                      //   the compensation terms of chunks v, v + n_val, ...
   int n_splits;       // gather workgroups per (sequence, KV head) (attend-only, dense)
   int pages_per_split;
   int dtype;          // 0 = bf16, 1 = f32
@@ -99,6 +101,13 @@ hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const voi
                                   const int32_t* block_table, const int32_t* seq_lens,
                                   int append_only, const Summ& out, hipStream_t stream);
 
+// Decode append: writes the new key and value rows (k_new, v_new:
+// [B][Hkv][D]) of every sequence's last token into its page and recomputes
+// that block's summary.
+hipError_t launch_append_tokens(const Shape& s, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                const Summ& out, hipStream_t stream);
+
 // One launch of the decode-step kernel in the given mode (not kModeFused).
 hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w, hipStream_t stream);
 
@@ -106,9 +115,10 @@ hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w
 // (0 if the kernel cannot run with this shape).
 int fused_resident_workgroups(const Shape& s);
 
-// One launch of the fused step kernel; s.bg_round must be set, with
-// s.bg_round * s.n_chunks <= fused_resident_workgroups(s), and with n_xcd > 0
-// ceil(bg_round / n_xcd) * 2 * n_chunks <= fused_resident_workgroups(s) / n_xcd.
+// One launch of the fused step kernel; s.bg_round and s.n_val must be set,
+// with W = n_chunks + n_val workgroups per pair:
+// s.bg_round * W <= fused_resident_workgroups(s), and with n_xcd > 0
+// ceil(bg_round / n_xcd) * W <= fused_resident_workgroups(s) / n_xcd.
 hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t stream);
 
 // Number of XCDs if the device sends workgroup i of a launch to XCD

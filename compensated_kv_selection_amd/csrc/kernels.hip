@@ -46,12 +46,15 @@ constexpr int kThreads = 256;
 // Summary build: mean key, mean value, grouped key variance, count of one
 // block for every KV head.  One workgroup per (sequence, block); threads over
 // (KV head, 8-channel slice).  Summaries are stored by logical block.
+// With kn (append only): the sequence's last token is new; its key and value
+// rows (kn, vn: [B][Hkv][D]) are written into the page and used in place of
+// what the page held there.
 // ---------------------------------------------------------------------------
 template <typename KV, int D>
 __global__ __launch_bounds__(kThreads) void summary_kernel(
-    Shape s, const KV* __restrict__ kc, const KV* __restrict__ vc, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ sl, int append_only, KV* __restrict__ mk, KV* __restrict__ mv,
-    float* __restrict__ gv, int32_t* __restrict__ cnt) {
+    Shape s, KV* kc, KV* vc, const int32_t* __restrict__ bt, const int32_t* __restrict__ sl,
+    int append_only, const KV* __restrict__ kn, const KV* __restrict__ vn, KV* __restrict__ mk,
+    KV* __restrict__ mv, float* __restrict__ gv, int32_t* __restrict__ cnt) {
   extern __shared__ float var_sh[];  // [Hkv][D] per-channel variances
   constexpr int LPR = D / 8;
   const int b = append_only ? (int)blockIdx.x : (int)blockIdx.x / s.max_blocks;
@@ -77,10 +80,18 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
     const bool isv = item >= nk;
     const int it = isv ? item - nk : item;
     const int g = it / LPR, c = it % LPR;
-    const KV* p = (isv ? vc : kc) + ((size_t)page * s.Hkv + g) * s.bs * D + c * 8;
+    KV* p = (isv ? vc : kc) + ((size_t)page * s.Hkv + g) * s.bs * D + c * 8;
     Raw8<KV> raw[kBlockSize];
 #pragma unroll
     for (int t = 0; t < kBlockSize; ++t) raw_load(p + t * D, raw[t]);
+    if (kn) {  // the new token is row n - 1; only this thread touches its 8 channels
+      Raw8<KV> nr;
+      raw_load((isv ? vn : kn) + ((size_t)b * s.Hkv + g) * D + c * 8, nr);
+      raw_store(p + (n - 1) * D, nr);
+#pragma unroll
+      for (int t = 0; t < kBlockSize; ++t)
+        if (t == n - 1) raw[t] = nr;
+    }
     float x0[8], sx[8], x[8];
     raw_float(raw[0], x0);
 #pragma unroll
@@ -832,18 +843,18 @@ __global__ __launch_bounds__(kThreads) void step_kernel(Shape s, StepIO io, Work
 
 // ---- launchers --------------------------------------------------------------
 
-hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const void* v_cache,
-                                  const int32_t* bt, const int32_t* sl, int append_only,
-                                  const Summ& o, hipStream_t st) {
+static hipError_t launch_summary(const Shape& s, void* k_cache, void* v_cache, const int32_t* bt,
+                                 const int32_t* sl, int append_only, const void* k_new,
+                                 const void* v_new, const Summ& o, hipStream_t st) {
   const int LPR = s.D / 8;
   int threads = ((s.Hkv * LPR + 63) / 64) * 64;
   threads = threads > kThreads ? kThreads : threads;
   const dim3 grid(append_only ? s.B : s.B * s.max_blocks);
   const size_t lds = (size_t)s.Hkv * s.D * sizeof(float);
-#define CKV_SUMM(KV, DD)                                                                        \
-  hipLaunchKernelGGL((summary_kernel<KV, DD>), grid, dim3(threads), lds, st, s,                 \
-                     (const KV*)k_cache, (const KV*)v_cache, bt, sl, append_only, (KV*)o.mean_k, \
-                     (KV*)o.mean_v, o.gvar, o.count)
+#define CKV_SUMM(KV, DD)                                                                          \
+  hipLaunchKernelGGL((summary_kernel<KV, DD>), grid, dim3(threads), lds, st, s, (KV*)k_cache,     \
+                     (KV*)v_cache, bt, sl, append_only, (const KV*)k_new, (const KV*)v_new,       \
+                     (KV*)o.mean_k, (KV*)o.mean_v, o.gvar, o.count)
   if (s.dtype == 0) {
     if (s.D == 128) CKV_SUMM(uint16_t, 128); else CKV_SUMM(uint16_t, 64);
   } else {
@@ -851,6 +862,20 @@ hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const voi
   }
 #undef CKV_SUMM
   return hipGetLastError();
+}
+
+hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const void* v_cache,
+                                  const int32_t* bt, const int32_t* sl, int append_only,
+                                  const Summ& o, hipStream_t st) {
+  // read only: the caches are written only when new tokens are given
+  return launch_summary(s, const_cast<void*>(k_cache), const_cast<void*>(v_cache), bt, sl, append_only,
+                        nullptr, nullptr, o, st);
+}
+
+hipError_t launch_append_tokens(const Shape& s, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const int32_t* bt, const int32_t* sl, const Summ& o,
+                                hipStream_t st) {
+  return launch_summary(s, k_cache, v_cache, bt, sl, 1, k_new, v_new, o, st);
 }
 
 // Calls f(kernel) with the step-kernel instance for (dtype, D, G) in MODE.

@@ -155,6 +155,14 @@ __device__ __forceinline__ void raw_load(const Buf& b, uint32_t e, Raw8<float>& 
   r.a = b.u128(4 * e);
   r.b = b.u128(4 * e + 16);
 }
+__device__ __forceinline__ void raw_store(uint16_t* p, const Raw8<uint16_t>& r) {
+  *reinterpret_cast<uint4*>(p) = r.a;
+}
+__device__ __forceinline__ void raw_store(float* p, const Raw8<float>& r) {
+  uint4* q = reinterpret_cast<uint4*>(p);
+  q[0] = r.a;
+  q[1] = r.b;
+}
 __device__ __forceinline__ void raw_zero(Raw8<uint16_t>& r) { r.a = make_uint4(0u, 0u, 0u, 0u); }
 __device__ __forceinline__ void raw_zero(Raw8<float>& r) { r.a = r.b = make_uint4(0u, 0u, 0u, 0u); }
 __device__ __forceinline__ void raw_float(const Raw8<uint16_t>& r, float (&x)[8]) {

@@ -131,6 +131,23 @@ ckv_status ckv_build_summaries(const ckv_dims* dims, const void* k_cache, const 
                                int32_t append_only, const ckv_summaries* summaries,
                                void* stream);
 
+/* Decode append in one launch (review FAQ: summaries are updated as tokens
+ * enter the cache): the last token of every sequence b, at position
+ * seq_lens[b] - 1 (seq_lens already count it), is new.  Its key
+ * k_new[b][g][0..d) and value v_new[b][g][0..d) (kv_dtype, [B][Hkv][d],
+ * contiguous) are written into slot (seq_lens[b] - 1) % block_size of page
+ * block_table[b][(seq_lens[b] - 1) / block_size] of k_cache and v_cache, and
+ * that block's summary is recomputed from its tokens.  Gives the same caches
+ * and summaries, bit for bit, as writing the token and then calling
+ * ckv_build_summaries with append_only != 0.  Sequences with seq_lens[b] == 0
+ * or a negative page id are left alone.  k_new and v_new must not overlap the
+ * caches; the caller owns every buffer.
+ * Errors: CKV_ERR_INVALID_ARG / CKV_ERR_UNSUPPORTED for bad dims or null
+ * pointers (nothing enqueued); CKV_ERR_HIP if the launch fails. */
+ckv_status ckv_append_tokens(const ckv_dims* dims, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const ckv_summaries* summaries, void* stream);
+
 /* Bytes of device workspace that ckv_score_select,
  * ckv_compensated_decode_attention and ckv_decode_step need for these dims
  * and this budget (0 when dims are invalid).  The same workspace must be

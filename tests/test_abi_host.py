@@ -84,6 +84,7 @@ def test_bad_dims_rejected_everywhere(lib, kw, status, needle):
     s = summ()
     calls = [
         lambda: lib.ckv_build_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(s), None),
+        lambda: lib.ckv_append_tokens(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), None),
         lambda: lib.ckv_score_select(ctypes.byref(d), FAKE, ctypes.byref(s), FAKE, FAKE, 512, 0, FAKE,
                                      FAKE, None, FAKE, 1 << 40, None),
         lambda: lib.ckv_compensated_decode_attention(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(s),
@@ -119,6 +120,12 @@ def test_null_pointers_rejected(lib):
     assert lib.ckv_build_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, None) == INVALID
     bad_s = C.CkvSummaries(0x100000, 0, 0x100000, 0x100000)
     assert lib.ckv_build_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(bad_s), None) == INVALID
+    for i in range(6):  # k_new, v_new, k_cache, v_cache, block_table, seq_lens
+        args = [FAKE] * 6
+        args[i] = n
+        assert lib.ckv_append_tokens(ctypes.byref(d), *args, ctypes.byref(s), None) == INVALID
+    assert lib.ckv_append_tokens(ctypes.byref(d), *([FAKE] * 6), None, None) == INVALID
+    assert lib.ckv_append_tokens(None, *([FAKE] * 6), ctypes.byref(s), None) == INVALID
     assert lib.ckv_score_select(ctypes.byref(d), n, ctypes.byref(s), FAKE, FAKE, 512, 0, FAKE, FAKE, None,
                                 FAKE, W, None) == INVALID
     assert lib.ckv_score_select(ctypes.byref(d), FAKE, ctypes.byref(s), FAKE, FAKE, 512, 0, n, FAKE, None,

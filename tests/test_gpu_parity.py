@@ -229,6 +229,28 @@ def test_fused_step_both_placements(across_xcds, monkeypatch):
     full_check(W.make_preset("llama_32k", seed=3), fused=True)
 
 
+@pytest.mark.parametrize("across_xcds", [False, True])
+def test_value_workgroups_take_several_chunks(across_xcds, monkeypatch):
+    # 16 (sequence, KV head) pairs of 21 chunks do not fit on the device with
+    # a value workgroup per chunk (16 x 42 > 2 x 256); with one value
+    # workgroup per about two chunks they fit in one round.  The shorter
+    # sequence leaves its last chunk empty.
+    if across_xcds:
+        monkeypatch.setenv("CKV_FUSED_ACROSS_XCDS", "1")
+    w = W.make_decode_inputs(name="two_seq_86k", seq_lens=[86000, 80000], num_q_heads=32, num_kv_heads=8,
+                             head_dim=128, r_groups=4, budget_tokens=512, dtype="bf16", n_needles=16,
+                             n_outliers=4, seed=11)
+    assert C.decode_step_launches(dims_of(w), 512) == 1
+    full_check(w, fused=True)
+
+
+def test_128k_with_spare_pages():
+    # 131077 tokens in a page table with room for 64 more: 33 chunks per
+    # pair, the last holding one block; two value workgroups take two chunks.
+    w = W.make_preset("llama_128k", seed=2, seq_lens=[131077], extra_capacity_tokens=64)
+    full_check(w, fused=True)
+
+
 def test_headline_shape_runs_as_one_launch():
     # 128K tokens, Hq 32, Hkv 8, d 128, 16-token blocks, 512-token budget
     dims = C.Dims(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, r_groups=4,
@@ -303,3 +325,88 @@ def test_prefill_then_decode_loop():
             assert np.abs(lse.cpu().numpy()[0] - l2).max() <= 1e-4
             M = -(-(L + 1) // 16)
             assert summ.count[0, M - 1].item() == osumm.count[M - 1]
+
+
+def test_decode_loop_graph_replays_match_eager():
+    # Prefill over 128K tokens, then the 64-step appending loop (2048-token
+    # budget) captured into one HIP graph: every replay, with eager work and
+    # synchronisations between replays, gives the eager loop's outputs bit
+    # for bit and leaves the workspace ready for the next call.
+    from compensated_kv_selection_amd.decode_loop import DecodeLoop
+    w = W.make_preset("prefill_128k_loop", seed=0)
+    steps = W.make_append_steps(w, 64, seed=21)
+    kc, vc = w.paged_cache()
+    dev = to_device(w, k_cache=kc, v_cache=vc)
+    del kc, vc
+    dims = dev.dims
+    summ = C.allocate_summaries(dims, "cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
+    loop = DecodeLoop(dev, summ, w.block_table, w.seq_lens, steps, w.dtype)
+    print(f"[case] decode loop eager: L0={int(w.seq_lens[0])} steps=64 budget={w.budget_tokens} "
+          f"launches={C.decode_step_launches(dims, w.budget_tokens)}", flush=True)
+    loop.run()
+    torch.cuda.synchronize()
+    outs = (loop.out, loop.lse, loop.num_selected, loop.selected)
+    ref = [x.clone() for x in outs]
+    assert torch.all(ref[2] == w.budget_tokens // 16)
+    assert torch.isfinite(ref[0]).all() and torch.isfinite(ref[1]).all()
+    print("[case] decode loop capture", flush=True)
+    g = loop.capture()
+    for rep in range(3):
+        for x in outs:
+            x.fill_(-7)
+        junk = torch.randn(1 << 20, device="cuda:0")
+        float(junk.square().sum())
+        torch.cuda.synchronize()
+        print(f"[case] decode loop replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("out", "lse", "num_selected", "selected"), outs, ref):
+            assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager loop"
+        check_workspace_clean(loop.ws, dims, w.budget_tokens)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_append_tokens_matches_write_then_append(dtype, d):
+    # New tokens landing at slot 8, 0, 15, 1, 0 and 15 of their blocks, and
+    # a sequence of length 0 that must be left alone: ckv_append_tokens gives
+    # the caches and summaries of writing the token and then running the
+    # append-mode summary build, bit for bit.
+    before = [1000, 768, 15, 1, 4096, 31]
+    w = W.make_decode_inputs(name="append", seq_lens=before, num_q_heads=8, num_kv_heads=2, head_dim=d,
+                             r_groups=4, budget_tokens=64, dtype=dtype, n_needles=0, n_outliers=2,
+                             extra_capacity_tokens=16, seed=31)
+    dev = to_device(w)
+    dims = dev.dims
+    summ = C.allocate_summaries(dims, "cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
+    rng = np.random.default_rng(32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k_new = torch.from_numpy(rng.standard_normal((6, 2, d), dtype=np.float32)).to("cuda:0", tdt)
+    v_new = torch.from_numpy(rng.standard_normal((6, 2, d), dtype=np.float32)).to("cuda:0", tdt)
+    after = torch.tensor([L + 1 for L in before[:-1]] + [0], dtype=torch.int32, device="cuda:0")
+
+    def state():
+        return (dev.k_cache.clone(), dev.v_cache.clone(),
+                C.Summaries(summ.mean_k.clone(), summ.mean_v.clone(), summ.gvar.clone(), summ.count.clone()))
+
+    ka, va, sa = state()
+    for b, L in enumerate(before[:-1]):
+        p, slot = int(w.block_table[b, L // 16]), L % 16
+        ka[p, :, slot, :] = k_new[b]
+        va[p, :, slot, :] = v_new[b]
+    C.build_summaries(dims, ka, va, dev.block_table, after, sa, append_only=True)
+    kb, vb, sb = state()
+    print(f"[case] append_tokens {dtype} d={d} lens={before}", flush=True)
+    C.append_tokens(dims, k_new, v_new, kb, vb, dev.block_table, after, sb)
+    torch.cuda.synchronize()
+
+    def bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+    assert torch.equal(bits(ka), bits(kb)) and torch.equal(bits(va), bits(vb))
+    assert torch.equal(bits(dev.k_cache[int(w.block_table[5, 1])]), bits(kb[int(w.block_table[5, 1])]))
+    for x, y in zip((sa.mean_k, sa.mean_v, sa.gvar, sa.count), (sb.mean_k, sb.mean_v, sb.gvar, sb.count)):
+        assert torch.equal(bits(x), bits(y))
+    # the tail blocks did change
+    assert not torch.equal(bits(summ.mean_k), bits(sb.mean_k))
