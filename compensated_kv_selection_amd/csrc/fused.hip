@@ -31,9 +31,9 @@
 //   a value workgroup waits for a chunk's weights, streams the chunk's mean
 //     values, sums the compensation terms of all the chunk's blocks and
 //     publishes them for the chunk's control workgroup.
-// Then every workgroup of the pair merges its slice of the pair's output from
-// the control workgroups' partials; the last to finish clears the pair's
-// headers and candidates and advances its epoch.
+// Then every control workgroup of the pair merges its slice of the pair's
+// output from the control workgroups' partials; the last to finish clears the
+// pair's headers and candidates and advances its epoch.
 // A wave's memory counter drains in issue order, so the long mean-value
 // stream lives in workgroups that never wait on small hand-offs, and it
 // starts once the mean keys have arrived, so that the ranking does not wait
@@ -801,10 +801,12 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup `slot` (of the pair's n_chunks + n_val) merges its slice of the
-// pair's output from the partials of the pair's control workgroups (each
-// holding its chunk's compensation sums too), waiting for each to carry this
-// call's tag.  The last workgroup to finish resets the pair for the next call.
+// Control workgroup `slot` of the pair merges its slice of the pair's output
+// from the partials of all the pair's control workgroups (each holding its
+// chunk's compensation sums too), waiting for each to carry this call's tag.
+// The value workgroups take no part: once their sums are published they
+// leave, instead of polling beside the control workgroups on the same CUs.
+// The last workgroup to finish resets the pair for the next call.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int bg, int slot, uint32_t epoch,
@@ -815,8 +817,8 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t tag = epoch + 1u;
   uint32_t* err = w.ctrl + 2;
-  const int nm = s.n_chunks + s.n_val;  // merging workgroups of the pair
-  const int np = s.n_chunks;            // partials: one per chunk (value sums folded in)
+  const int nm = s.n_chunks;  // merging workgroups of the pair
+  const int np = s.n_chunks;  // partials: one per chunk (value sums folded in)
   const int per = (NV + nm - 1) / nm;  // float4 outputs of this workgroup
   const int step = max(1, NT / np);    // outputs merged per pass
   const int o0 = slot * per, o1 = min(NV, o0 + per);
@@ -943,6 +945,8 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
     const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
     if (role < s.n_chunks) {
       ctl_chunk<KV, D, G>(s, io, w, bg, role, epoch + 1u, lds.c);
+      __syncthreads();
+      merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m, sh);
     } else {
       // value workgroup v sums chunks v, v + n_val, ... in turn
       for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
@@ -950,8 +954,6 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
         __syncthreads();
       }
     }
-    __syncthreads();
-    merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m, sh);
     __syncthreads();
   }
 }
