@@ -119,9 +119,9 @@ Layout layout(const ckv::Shape& s) {
   L.gpart = off;
   off += align_up(bg * s.n_splits * s.G * 2 * pst * sizeof(float));
   L.fhdr = off;
-  off += align_up(bg * s.n_chunks * s.G * sizeof(uint64_t));
+  off += align_up(2 * bg * s.n_chunks * s.G * sizeof(uint64_t));
   L.fcand = off;
-  off += align_up(bg * s.n_chunks * kcap * sizeof(uint64_t));
+  off += align_up(2 * bg * s.n_chunks * kcap * sizeof(uint64_t));
   L.fw = off;
   off += align_up(bg * s.n_chunks * s.G * (ckv::kChunk + 1) * sizeof(uint64_t));
   L.fpart = off;

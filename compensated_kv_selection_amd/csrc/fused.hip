@@ -141,6 +141,16 @@ __device__ __forceinline__ int fused_key_page(uint64_t key) {
   return p == kNoPage ? -1 : (int)p;
 }
 
+// Chunk headers and candidates are double-buffered by the parity of the
+// call's tag: a call publishes into its own half, and its value workgroups
+// clear the other half, which the previous call used and the next call uses.
+__device__ __forceinline__ uint64_t* hdr_half(const Shape& s, const Work& w, uint32_t tag) {
+  return w.fhdr + (size_t)(tag & 1u) * s.B * s.Hkv * s.n_chunks * s.G;
+}
+__device__ __forceinline__ uint64_t* cand_half(const Shape& s, const Work& w, uint32_t tag) {
+  return w.fcand + (size_t)(tag & 1u) * s.B * s.Hkv * s.n_chunks * max(s.kmax, 1);
+}
+
 // Copy n published 64-bit words into dst, waiting for each to become
 // nonzero.  Word e is read at index (e / per) * stride + e % per.  Each
 // thread's re-reads are bounded in total; running out sets the error word.
@@ -188,6 +198,16 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
                                 const Coh& part, uint32_t tag, const Coh* extra, uint32_t* err) {
   constexpr int LPR = D / 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = tid % LPR;
+  // the other partial's words for this thread's first output, requested
+  // before the reductions so that their round trip overlaps them
+  uint64_t x[4] = {0u, 0u, 0u, 0u};
+  if (extra && tid < G * D / 2) {
+    const int h = (tid / (D / 2)) * (D + 2), d2 = tid % (D / 2);
+    x[0] = extra->u64(h);
+    x[1] = extra->u64(h + 1);
+    x[2] = extra->u64(h + 2 + 2 * d2);
+    x[3] = extra->u64(h + 3 + 2 * d2);
+  }
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     uint32_t mb = __float_as_uint(m[j]);
@@ -232,8 +252,9 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
     const int h = j * (D + 2);
     if (extra) {
       uint32_t spins = 0;
-      const uint64_t w0 = extra->u64(h), w1 = extra->u64(h + 1), w2 = extra->u64(h + 2 + 2 * d2),
-                     w3 = extra->u64(h + 3 + 2 * d2);
+      const bool first = o == tid;
+      const uint64_t w0 = first ? x[0] : extra->u64(h), w1 = first ? x[1] : extra->u64(h + 1),
+                     w2 = first ? x[2] : extra->u64(h + 2 + 2 * d2), w3 = first ? x[3] : extra->u64(h + 3 + 2 * d2);
       const float me = read_tagged(*extra, h, w0, tag, spins, err);
       const float le = read_tagged(*extra, h + 1, w1, tag, spins, err);
       const float e0 = read_tagged(*extra, h + 2 + 2 * d2, w2, tag, spins, err);
@@ -423,7 +444,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 
   // ---- per head: chunk max, Z_hat part, compensation weights, log-scores ----
   if (need_mu) {
-    const Coh hdr(w.fhdr + (size_t)bg * s.n_chunks * G, (size_t)s.n_chunks * G * 8, s.n_xcd > 0);
+    const Coh hdr(hdr_half(s, w, tag) + (size_t)bg * s.n_chunks * G, (size_t)s.n_chunks * G * 8, s.n_xcd > 0);
     const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8, s.n_xcd > 0);
     for (int j = wave; j < G; j += NW) {
       float mx = -INFINITY;
@@ -458,7 +479,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     // log Z_hat per head from every chunk header of the pair
     const int nh = s.n_chunks * G;
     {
-      const Coh hdr(w.fhdr + (size_t)bg * nh, (size_t)nh * 8, s.n_xcd > 0);
+      const Coh hdr(hdr_half(s, w, tag) + (size_t)bg * nh, (size_t)nh * 8, s.n_xcd > 0);
       read_published(hdr, nh, nh, 0, L.u.keys, err);
     }
     __syncthreads();
@@ -487,7 +508,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       mykey = fused_key(S, start + tid, L.pgt[tid]);
     }
     // the chunk's top-k candidates, published largest first
-    const Coh cand(w.fcand + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8, s.n_xcd > 0);
+    const Coh cand(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8,
+                   s.n_xcd > 0);
     const int k1 = min(kk, nrows);
     const bool fast = kk <= 64;  // selections of up to one wave's width stay in registers
     if (fast) {
@@ -551,25 +573,20 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       if (nsurv <= 64) {
         listed = true;
         if (wave == 0) {
+          // lane e < kk holds the pair's e-th largest key; the chunks' workgroups
+          // attend to them round robin in that order
           const uint64_t top = wave_sort_desc(lane < (int)nsurv ? L.surv[lane] : 0ull);
           const int ti = fused_key_index(top);
-          const bool sel = lane < kk && ti >= 0 && ti < M;
-          // by block index, ascending: sort on the complemented index
-          const uint64_t a = wave_sort_desc(sel ? ((uint64_t)(0x3FFFu - (uint32_t)ti) << 32) |
-                                                      (uint32_t)fused_key_page(top)
-                                                : 0ull);
-          const bool real = (a >> 32) != 0;
-          const int bi = 0x3FFF - (int)(a >> 32), bp = (int)(uint32_t)a;
-          // lane e < kk holds the e-th selected block of the pair
+          const bool real = lane < kk && ti >= 0 && ti < M;
           if (real && lane % s.n_chunks == chunk) {
-            L.gblk[lane / s.n_chunks] = bi;
-            L.gpg[lane / s.n_chunks] = bp;
+            L.gblk[lane / s.n_chunks] = ti;
+            L.gpg[lane / s.n_chunks] = fused_key_page(top);
           }
-          const bool mine = real && bi >= start && bi < start + nrows;
+          const bool mine = real && ti >= start && ti < start + nrows;
           const uint64_t mb = __ballot(mine);
-          if (mine) L.own[__popcll(mb & ((1ull << lane) - 1ull))] = bi - start;
+          if (mine) L.own[__popcll(mb & ((1ull << lane) - 1ull))] = ti - start;
           if (lane == 0) L.nown = (uint32_t)__popcll(mb);
-          if (chunk == 0 && io.selected && lane < kk) io.selected[(size_t)bg * s.kmax + lane] = real ? bi : -1;
+          L.surv[lane] = real ? (uint64_t)ti : ~0ull;  // for the selection output, written last
         }
         __syncthreads();
         n_own = (int)L.nown;
@@ -722,7 +739,20 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     if (out) {
       for (int e = kk + tid; e < s.kmax; e += NT) out[e] = -1;
       if (ranked) {
-        if (!listed) emit_selection<NT>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
+        if (!listed) {
+          emit_selection<NT>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
+        } else if (wave == 0) {
+          // by ascending block index: a block's place is the number of selected
+          // blocks with a lower index (the indices differ)
+          const uint64_t sv = L.surv[lane];
+          const bool real = lane < kk && sv != ~0ull;
+          const int ti = (int)(uint32_t)sv;
+          const int nreal = __popcll(__ballot(real));  // the real entries come first
+          int rank = 0;
+          for (int e = 0; e < nreal; ++e) rank += __builtin_amdgcn_readlane(ti, e) < ti ? 1 : 0;
+          if (real) out[rank] = ti;
+          else if (lane >= nreal && lane < kk) out[lane] = -1;
+        }
       } else
         for (int i = tid; i < kk; i += NT) out[i] = i;
     }
@@ -881,18 +911,9 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
     }
     __syncthreads();
   }
-  // the last workgroup of the pair to finish resets it for the next call
+  // the last workgroup of the pair to finish resets its counter and
+  // advances its epoch
   if (arrive(ctr_done(w, bg), sh) != (uint32_t)(nm - 1)) return;
-  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
-  const int M = (Lseq + s.bs - 1) / s.bs;
-  const int kk = min(M, s.kmax);
-  if (kk > 0 && kk < M) {
-    const int nch = s.n_chunks;
-    const Coh hdr(w.fhdr + (size_t)bg * nch * G, (size_t)nch * G * 8, s.n_xcd > 0);
-    for (int e = tid; e < nch * G; e += NT) hdr.put_u64(e, 0u);
-    const Coh cand(w.fcand + (size_t)bg * nch * s.kmax, (size_t)nch * s.kmax * 8, s.n_xcd > 0);
-    for (int e = tid; e < nch * kk; e += NT) cand.put_u64((e / kk) * s.kmax + e % kk, 0u);
-  }
   if (tid == 0) {
     st_c(ctr_done(w, bg), 0u);
     st_c(ctr_epoch(w, bg), epoch + 1u);
@@ -952,6 +973,16 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
       for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
         val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
         __syncthreads();
+      }
+      // then clear its chunks' rows of the previous call's headers and
+      // candidates (tag `epoch`), for the next call
+      const int kc = max(s.kmax, 1);
+      for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
+        const Coh hdr(hdr_half(s, w, epoch) + ((size_t)bg * s.n_chunks + chunk) * G, (size_t)G * 8, s.n_xcd > 0);
+        if ((int)threadIdx.x < G) hdr.put_u64((int)threadIdx.x, 0u);
+        const Coh cand(cand_half(s, w, epoch) + ((size_t)bg * s.n_chunks + chunk) * kc, (size_t)kc * 8,
+                       s.n_xcd > 0);
+        for (int e = (int)threadIdx.x; e < kc; e += NT) cand.put_u64(e, 0u);
       }
     }
     __syncthreads();

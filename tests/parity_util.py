@@ -29,7 +29,7 @@ from compensated_kv_selection_amd import compkv as C
 from compensated_kv_selection_amd.tensors import to_device, torch_to_storage
 from compensated_kv_selection_amd.workloads import DecodeInputs
 from oracle import compkv_oracle as O
-from ws_layout import PUBLISHED_REGIONS, workspace_regions
+from ws_layout import PUBLISHED_REGIONS, published_row_words, workspace_regions
 
 NEAR_TIE = 1e-5
 OUT_ATOL = 2e-3
@@ -61,10 +61,18 @@ def check_workspace_clean(ws, dims, budget):
     regions = workspace_regions(dims.batch, dims.num_q_heads, dims.num_kv_heads, dims.head_dim,
                                 dims.max_blocks_per_seq, budget)
     assert sum(regions) == ws.numel(), (sum(regions), ws.numel())
+    epochs = C.workspace_control(ws, dims.batch, dims.num_kv_heads)[
+        C.CTRL_WORDS_HEADER + C.CTRL_EPOCH::C.CTRL_WORDS_PER_PAIR].tolist()
+    rows = published_row_words(dims.num_q_heads, dims.num_kv_heads, dims.max_blocks_per_seq, budget)
+    bgs = dims.batch * dims.num_kv_heads
     for r in PUBLISHED_REGIONS:
         lo = sum(regions[:r])
         words = ws[lo:lo + regions[r]].view(torch.int64).cpu()
-        assert int((words != 0).sum()) == 0, f"published words of region {r} not cleared"
+        n = rows[r]
+        for bg, ep in enumerate(epochs):
+            half = (ep + 1) % 2   # the half the next call publishes into
+            seg = words[(half * bgs + bg) * n:(half * bgs + bg + 1) * n]
+            assert int((seg != 0).sum()) == 0, f"published words of region {r}, pair {bg} not cleared"
 
 
 def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.SCORE_COMPKV,

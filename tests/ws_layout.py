@@ -19,8 +19,20 @@ def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
     n_splits = min(64, max(1, (kmax + 3) // 4))
     return [up((64 + 8 * bg) * 4), up(B * Hq * max_blocks * 4), up(bg * n_chunks * G * pst * 4),
             up(bg * n_slices * kcap * 8), up(bg * n_splits * G * 2 * pst * 4),
-            up(bg * n_chunks * G * 8), up(bg * n_chunks * kcap * 8),
+            up(2 * bg * n_chunks * G * 8), up(2 * bg * n_chunks * kcap * 8),
             up(bg * n_chunks * G * 257 * 8), up(bg * 2 * n_chunks * G * (D + 2) * 8)]
 
 
-PUBLISHED_REGIONS = (5, 6)   # fused chunk headers and candidates: zero between calls
+# Fused chunk headers ([2][B*Hkv][n_chunks][G] words) and candidates
+# ([2][B*Hkv][n_chunks][kcap] words): a call with tag t (the pair's epoch
+# counter before the call, plus one) publishes into half t % 2 and clears the
+# other half, so between calls half (epoch + 1) % 2 of every pair is zero.
+PUBLISHED_REGIONS = (5, 6)
+
+
+def published_row_words(Hq, Hkv, max_blocks, budget):
+    """Words per (pair, half) of the header and candidate regions."""
+    G = Hq // Hkv
+    n_chunks = -(-max_blocks // 256)
+    kcap = max(min(max_blocks, budget // 16), 1)
+    return {5: n_chunks * G, 6: n_chunks * kcap}
