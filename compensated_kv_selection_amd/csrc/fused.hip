@@ -749,7 +749,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           const int ti = (int)(uint32_t)sv;
           const int nreal = __popcll(__ballot(real));  // the real entries come first
           int rank = 0;
-          for (int e = 0; e < nreal; ++e) rank += __builtin_amdgcn_readlane(ti, e) < ti ? 1 : 0;
+          for (int e = 0; e < nreal; ++e) rank += (int)(uint32_t)L.surv[e] < ti ? 1 : 0;  // LDS broadcast
           if (real) out[rank] = ti;
           else if (lane >= nreal && lane < kk) out[lane] = -1;
         }
