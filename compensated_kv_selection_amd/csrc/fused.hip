@@ -32,15 +32,16 @@
 //     values, sums the compensation terms of all the chunk's blocks and
 //     publishes them for the chunk's control workgroup.
 // Then every control workgroup of the pair merges its slice of the pair's
-// output from the control workgroups' partials; the last to finish clears the
-// pair's headers and candidates and advances its epoch.
+// output from the control workgroups' partials, and chunk 0's advances the
+// pair's epoch.
 // A wave's memory counter drains in issue order, so the long mean-value
-// stream lives in workgroups that never wait on small hand-offs, and it
-// starts once the mean keys have arrived, so that the ranking does not wait
-// behind it.
+// stream lives in workgroups that never wait on small hand-offs; it starts
+// once the mean keys have arrived, so that the ranking does not wait behind
+// it, and it is paced, so that it does not slow the hand-offs.
 // Hand-offs are 64-bit words read with device-scope loads: headers and
-// candidates are never 0 once written (cleared after use); weights and
-// partials carry the call's epoch in their upper half.  Readers poll such
+// candidates are never 0 once written (double-buffered by the parity of the
+// call's tag, each half cleared during the call after the one that used it);
+// weights and partials carry the call's tag in their upper half.  Readers poll such
 // words directly, so publishing needs no completion wait.  When the device
 // sends workgroups to its XCDs round robin, all workgroups of a pair run on
 // one XCD and the words are stored with the default policy, so they are
@@ -117,7 +118,6 @@ union FusedLds {
 };
 
 __device__ __forceinline__ uint32_t* ctr_epoch(const Work& w, int bg) { return w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 3; }
-__device__ __forceinline__ uint32_t* ctr_done(const Work& w, int bg) { return w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 5; }
 
 __device__ __forceinline__ uint64_t tagged(float x, uint32_t tag) {
   return ((uint64_t)tag << 32) | __float_as_uint(x);
@@ -846,11 +846,10 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 // chunk's compensation sums too), waiting for each to carry this call's tag.
 // The value workgroups take no part: once their sums are published they
 // leave, instead of polling beside the control workgroups on the same CUs.
-// The last workgroup to finish resets the pair for the next call.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int bg, int slot, uint32_t epoch,
-                            MergeLds<D, G>& L, uint32_t* sh) {
+                            MergeLds<D, G>& L) {
   constexpr int NV = G * D / 4;
   const int b = bg / s.Hkv, g = bg % s.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -921,13 +920,10 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
     }
     __syncthreads();
   }
-  // the last workgroup of the pair to finish resets its counter and
-  // advances its epoch
-  if (arrive(ctr_done(w, bg), sh) != (uint32_t)(nm - 1)) return;
-  if (tid == 0) {
-    st_c(ctr_done(w, bg), 0u);
-    st_c(ctr_epoch(w, bg), epoch + 1u);
-  }
+  // Every partial of the pair carries this call's tag, so every workgroup of
+  // the pair has read the epoch: the workgroup of slot 0 (which reads every
+  // partial) advances it for the next call, without waiting for the others.
+  if (slot == 0 && tid == 0) st_c(ctr_epoch(w, bg), epoch + 1u);
 }
 
 // Brings every 64-byte line of the kernel's explicit arguments into the
@@ -947,7 +943,6 @@ __device__ __forceinline__ void warm_kernel_args() {
 template <typename KV, int D, int G>
 __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
   __shared__ FusedLds<D, G> lds;
-  __shared__ uint32_t sh[4];
   warm_kernel_args();
   // This workgroup's pair (of the round) and role: control workgroup of
   // chunk `role` (role < n_chunks), else value workgroup role - n_chunks.
@@ -977,7 +972,7 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
     if (role < s.n_chunks) {
       ctl_chunk<KV, D, G>(s, io, w, bg, role, epoch + 1u, lds.c);
       __syncthreads();
-      merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m, sh);
+      merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m);
     } else {
       // value workgroup v sums chunks v, v + n_val, ... in turn
       for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {

@@ -58,20 +58,20 @@ struct Shape {
 // Device pointers carved from the caller's workspace.
 struct Work {
   uint32_t* ctrl;  // [kCtrlHeader + kCtrlPerPair * B * Hkv]: error flag at 2; per (b, g):
-                   //   (spare), select arrivals, attend arrivals, fused epoch, fused
-                   //   arrivals, fused merges done, (spare x2)
+                   //   (spare), select arrivals, attend arrivals, fused epoch, (spare x4)
   float* xs;       // [B][Hq][max_blocks]  exp(log score - chunk max of log score)
   float* cpart;    // [B][Hkv][n_chunks][G][D+4]  per chunk and head: max s_bar, sum w,
                    //   sum w (1 + var_hat/2), max log score, sum w mean_v; w = n e^{s_bar - max}
   uint64_t* cand;  // [B][Hkv][n_slices][kmax] first-level top-k candidates
   float* gpart;    // [B][Hkv][n_splits][G][2][D+4] exact-token partials and the selected
                    //   blocks' own compensation terms
-  uint64_t* fhdr;  // [B][Hkv][n_chunks][G] fused: chunk header (max s_bar, Z_hat part), 0 = unset
-  uint64_t* fcand; // [B][Hkv][n_chunks][kmax] fused: chunk candidates, 0 = unset
+  uint64_t* fhdr;  // [2][B][Hkv][n_chunks][G] fused: chunk header (max s_bar, Z_hat part),
+                   //   0 = unset; half = parity of the call's tag
+  uint64_t* fcand; // [2][B][Hkv][n_chunks][kmax] fused: chunk candidates, 0 = unset
   uint64_t* fw;    // [B][Hkv][n_chunks][G][kChunk + 1] fused: compensation weights and chunk
-                   //   max, epoch-tagged
+                   //   max, tagged
   uint64_t* fpart; // [B][Hkv][2 * n_chunks][G][D+2] fused: control and value partials
-                   //   (max, sum, acc[D]), epoch-tagged
+                   //   (max, sum, acc[D]), tagged
 };
 
 struct Summ {
