@@ -175,6 +175,52 @@ def sweep(args, dev0) -> int:
     return 0
 
 
+def sweep_r(args, dev0) -> int:
+    """Step latency over the number of variance groups r (1, 2, 4, 8, 16,
+    128 = d) at 128K context and a 512-token budget, for the CompKV score and
+    for estimated-mass selection with compensation (the decoupled baseline).
+    Steps rotate over layer copies whose summaries exceed the last-level
+    cache; graph replay."""
+    import torch
+    from compensated_kv_selection_amd import compkv as C
+    from compensated_kv_selection_amd import workloads as W
+    from compensated_kv_selection_amd.tensors import to_device
+
+    w = W.make_preset("llama_128k", seed=args.seed)
+    base = to_device(w, dev0)
+    M = -(-131072 // 16)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev0)
+    lse = torch.empty((1, 32), dtype=torch.float32, device=dev0)
+    sel = torch.empty((1, 8, 32), dtype=torch.int32, device=dev0)
+    nsel = torch.empty((1, 8), dtype=torch.int32, device=dev0)
+    for r in (1, 2, 4, 8, 16, 128):
+        dims = dataclasses.replace(base.dims, r_groups=r)
+        n_layers = 16
+        layers = []
+        for li in range(n_layers):
+            kc = base.k_cache if li == 0 else base.k_cache.clone()
+            vc = base.v_cache if li == 0 else base.v_cache.clone()
+            summ = C.allocate_summaries(dims, dev0)
+            C.build_summaries(dims, kc, vc, base.block_table, base.seq_lens, summ)
+            layers.append((kc, vc, summ))
+        torch.cuda.synchronize()
+        ws = C.allocate_workspace(C.workspace_bytes(dims, 512), dev0)
+        res = {}
+        for name, mode in (("compkv", C.SCORE_COMPKV), ("mass_hat_compensated", C.SCORE_MASS)):
+            def step(i, mode=mode):
+                kc, vc, summ = layers[i % n_layers]
+                C.decode_step(dims, base.q, kc, vc, summ, base.block_table, base.seq_lens, 512, ws, mode,
+                              selected=sel, num_selected=nsel, out=out, lse=lse)
+            res[name] = round(graph_time_us(torch, step, 100), 2)
+        summary_bytes = M * 8 * (2 * 128 * 2 + 4 * r) + 4 * M
+        print(json.dumps({"sweep": "decode step latency over r", "seq_len": 131072, "budget_tokens": 512,
+                          "r_groups": r, "us_per_step": res, "algorithmic_bytes": summary_bytes + 8 * 32 * 8192,
+                          "layer_copies": n_layers, "data": "synthetic"}), flush=True)
+        del layers
+        torch.cuda.empty_cache()
+    return 0
+
+
 def decode_loop(args, dev0) -> int:
     """Prefill plus a generation loop at 128K context (Llama-3.1-8B layer
     shape): the bulk summary build over 131072 tokens, then 64 decode steps,
@@ -261,6 +307,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="only time the step over context lengths 32K, 64K, 128K x budgets 512, 1024, 2048 "
                          "tokens (Llama-3.1-8B layer shape), with dense decode per length; one JSON line each")
+    ap.add_argument("--sweep-r", action="store_true",
+                    help="only time the step at 128K / 512 for r = 1, 2, 4, 8, 16, 128 variance groups, "
+                         "CompKV and estimated-mass selection; one JSON line per r")
     ap.add_argument("--decode-loop", action="store_true",
                     help="only time the prefill summary build and a 64-step appending decode loop at 128K "
                          "context, 2048-token budget, captured into one HIP graph; one JSON line")
@@ -307,6 +356,8 @@ def main() -> int:
         return sweep(args, dev0)
     if args.decode_loop:
         return decode_loop(args, dev0)
+    if args.sweep_r:
+        return sweep_r(args, dev0)
     t_gen = time.time()
     w = W.make_preset(args.workload, seed=args.seed)
     print(f"[bench] generated {args.workload} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)

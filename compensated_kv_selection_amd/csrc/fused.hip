@@ -277,7 +277,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
 // ---------------------------------------------------------------------------
 // Control workgroup of chunk `chunk` of pair bg.
 // ---------------------------------------------------------------------------
-template <typename KV, int D, int G>
+template <typename KV, int D, int G, bool kR4>
 __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
                           CtlLds<D, G>& L) {
   constexpr int LPR = D / 8, RS = NT / LPR;
@@ -314,7 +314,11 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   const int pge = (int)btb.u32(4 * tid);
   bf16x8_t qa[KT];
   uint4 mu[NMU];
-  float4 gpre[4];
+  // Grouped variances in registers: with r = 4 the four rows of this lane's
+  // matrix-core results (16 bytes each); otherwise this thread's block row
+  // (row tid of the chunk) when r <= 16, else read later from memory.
+  constexpr int kRReg = 16;
+  float gvr[kRReg];
   const bool holder = (lane >> 4) * 4 < G;
   if constexpr (MF) {
     const int head = lane & 15, kq = lane >> 4;
@@ -326,8 +330,28 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       const int row = 64 * wave + RPI * u + lane / CPR;
       mu[u] = mkb.u128(2 * (row * D + (lane % CPR) * 8));
     }
+    if constexpr (kR4) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) gpre[u] = gvb.f128(16 * (64 * wave + 16 * u + (lane & 15)));
+      for (int u = 0; u < 4; ++u) {
+        const float4 v = gvb.f128(16 * (64 * wave + 16 * u + (lane & 15)));
+        gvr[4 * u] = v.x;
+        gvr[4 * u + 1] = v.y;
+        gvr[4 * u + 2] = v.z;
+        gvr[4 * u + 3] = v.w;
+      }
+    } else if (r < 4) {  // r in {1, 2}: the row's r floats
+#pragma unroll
+      for (int e = 0; e < kRReg; ++e) gvr[e] = e < r ? __uint_as_float(gvb.u32(4 * (tid * r + e))) : 0.f;
+    } else {  // r a multiple of 4: up to 16 floats in 16-byte pieces
+#pragma unroll
+      for (int q = 0; q < kRReg / 4; ++q) {
+        const float4 v = 4 * q < r && r <= kRReg ? gvb.f128(4 * (tid * r + 4 * q)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        gvr[4 * q] = v.x;
+        gvr[4 * q + 1] = v.y;
+        gvr[4 * q + 2] = v.z;
+        gvr[4 * q + 3] = v.w;
+      }
+    }
   }
   // q rows to LDS; partial |q|^2 of each thread's 8 channels
   {
@@ -391,20 +415,44 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           for (int i = 0; i < 4; ++i) {
             const int j = 4 * (lane >> 4) + i;
             if (j < G) {
-              float sig = 0.f;
-              if (ranked) {
-                if (r == 4) {
-                  sig = fmaf(L.qn[j * 4 + 0], gpre[g4].x, sig);
-                  sig = fmaf(L.qn[j * 4 + 1], gpre[g4].y, sig);
-                  sig = fmaf(L.qn[j * 4 + 2], gpre[g4].z, sig);
-                  sig = fmaf(L.qn[j * 4 + 3], gpre[g4].w, sig);
-                } else {
-                  for (int e = 0; e < r; ++e) sig = fmaf(L.qn[j * r + e], gv[(size_t)ri * r + e], sig);
+              L.sb[j][ri] = acc[i] * s.tau;
+              if constexpr (kR4) {  // variance estimate: sum_t |q_t|^2 gvar_t
+                float sig = 0.f;
+                if (ranked) {
+                  sig = fmaf(L.qn[j * 4 + 0], gvr[4 * g4 + 0], sig);
+                  sig = fmaf(L.qn[j * 4 + 1], gvr[4 * g4 + 1], sig);
+                  sig = fmaf(L.qn[j * 4 + 2], gvr[4 * g4 + 2], sig);
+                  sig = fmaf(L.qn[j * 4 + 3], gvr[4 * g4 + 3], sig);
+                }
+                L.lam[j][ri] = sig * s.tau2;
+              }
+            }
+          }
+        }
+      }
+      if constexpr (!kR4) {
+        // the variance estimate of row tid for every head, from the row's
+        // variances in registers (r <= 16) or memory
+        if (tid < nrows) {
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            float sig = 0.f;
+            if (ranked) {
+              if (r <= kRReg) {
+#pragma unroll
+                for (int e = 0; e < kRReg; ++e)
+                  if (e < r) sig = fmaf(L.qn[j * r + e], gvr[e], sig);
+              } else {
+                for (int q = 0; q < r / 4; ++q) {
+                  const float4 v = gvb.f128(4 * (tid * r + 4 * q));
+                  sig = fmaf(L.qn[j * r + 4 * q], v.x, sig);
+                  sig = fmaf(L.qn[j * r + 4 * q + 1], v.y, sig);
+                  sig = fmaf(L.qn[j * r + 4 * q + 2], v.z, sig);
+                  sig = fmaf(L.qn[j * r + 4 * q + 3], v.w, sig);
                 }
               }
-              L.sb[j][ri] = acc[i] * s.tau;
-              L.lam[j][ri] = sig * s.tau2;
             }
+            L.lam[j][tid] = sig * s.tau2;
           }
         }
       }
@@ -940,7 +988,7 @@ __device__ __forceinline__ void warm_kernel_args() {
   asm volatile("" ::"s"(x));
 }
 
-template <typename KV, int D, int G>
+template <typename KV, int D, int G, bool kR4>
 __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
   __shared__ FusedLds<D, G> lds;
   warm_kernel_args();
@@ -970,7 +1018,7 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
   for (int bg = pair; bg < s.B * s.Hkv; bg += s.bg_round) {
     const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
     if (role < s.n_chunks) {
-      ctl_chunk<KV, D, G>(s, io, w, bg, role, epoch + 1u, lds.c);
+      ctl_chunk<KV, D, G, kR4>(s, io, w, bg, role, epoch + 1u, lds.c);
       __syncthreads();
       merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m);
     } else {
@@ -994,20 +1042,27 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
   }
 }
 
-// Calls f(kernel, index) with the fused kernel instance for (dtype, D, G).
+// Calls f(kernel, index) with the fused kernel instance for (dtype, D, G,
+// r == 4); index < 32.  bf16 has a separate instance for r == 4, which keeps
+// the variances of the rows of its matrix-core results in registers; f32
+// scores on the vector ALU and reads them from memory whatever r is.
 template <class F>
 auto with_fused(const Shape& s, F&& f) {
-#define CKV_G(KV, DD)                                          \
-  switch (s.G) {                                               \
-    case 1: return f(&fused_step_kernel<KV, DD, 1>, 0);        \
-    case 2: return f(&fused_step_kernel<KV, DD, 2>, 1);        \
-    case 4: return f(&fused_step_kernel<KV, DD, 4>, 2);        \
-    default: return f(&fused_step_kernel<KV, DD, 8>, 3);       \
+#define CKV_G(KV, DD, R4, I)                                           \
+  switch (s.G) {                                                       \
+    case 1: return f(&fused_step_kernel<KV, DD, 1, R4>, (I) + 0);      \
+    case 2: return f(&fused_step_kernel<KV, DD, 2, R4>, (I) + 1);      \
+    case 4: return f(&fused_step_kernel<KV, DD, 4, R4>, (I) + 2);      \
+    default: return f(&fused_step_kernel<KV, DD, 8, R4>, (I) + 3);     \
   }
   if (s.dtype == 0) {
-    if (s.D == 128) { CKV_G(uint16_t, 128) } else { CKV_G(uint16_t, 64) }
+    if (s.r == 4) {
+      if (s.D == 128) { CKV_G(uint16_t, 128, true, 0) } else { CKV_G(uint16_t, 64, true, 4) }
+    } else {
+      if (s.D == 128) { CKV_G(uint16_t, 128, false, 8) } else { CKV_G(uint16_t, 64, false, 12) }
+    }
   } else {
-    if (s.D == 128) { CKV_G(float, 128) } else { CKV_G(float, 64) }
+    if (s.D == 128) { CKV_G(float, 128, true, 16) } else { CKV_G(float, 64, true, 20) }
   }
 #undef CKV_G
 }
@@ -1020,10 +1075,9 @@ int fused_resident_workgroups(const Shape& s) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   // occupancy per (device, kernel instance), computed once
   constexpr int kDevices = 64;
-  static int cache[kDevices][16];
-  const int variant = (s.dtype == 0 ? 0 : 8) + (s.D == 128 ? 0 : 4);
-  return with_fused(s, [&](auto fn, int gi) {
-    int* slot = dev < kDevices ? &cache[dev][variant + gi] : nullptr;
+  static int cache[kDevices][32];
+  return with_fused(s, [&](auto fn, int vi) {
+    int* slot = dev < kDevices ? &cache[dev][vi] : nullptr;
     int per_cu = slot ? __atomic_load_n(slot, __ATOMIC_RELAXED) : 0;
     if (per_cu <= 0) {
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0) != hipSuccess) per_cu = 0;
