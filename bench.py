@@ -282,8 +282,8 @@ def decode_loop(args, dev0) -> int:
                       "budget_tokens": w.budget_tokens, "layer_copies": n_layers,
                       "prefill_build_us": round(float(np.median(build_ms)) * 1e3, 1),
                       "us_per_layer_step": round(us, 2),
-                      "per_layer_step": "length and query copies, ckv_append_tokens (new key and value "
-                                        "into their page, tail-block summary), ckv_decode_step",
+                      "per_layer_step": "ckv_append_tokens (new key and value into their page, "
+                                        "tail-block summary), then ckv_decode_step",
                       "launches_per_decode_step": C.decode_step_launches(dims, w.budget_tokens),
                       "data": "synthetic"}), flush=True)
     return 0

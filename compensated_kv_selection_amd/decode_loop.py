@@ -1,14 +1,13 @@
 """A generation loop over one paged attention layer: every step appends one
 token per sequence and runs the compensated decode step on the grown context.
 
-Per step: seq_lens grow by one and the new query is copied in; one
-ckv_append_tokens launch writes every sequence's new key and value into the
-page slot its block table gives for the new position and recomputes that
-block's summary; then ckv_decode_step scores, selects and attends.  All
-per-step inputs (queries, new keys and values, lengths)
-are staged on the device up front and every step writes its own output
-buffers, so any run of steps can be captured into one HIP graph and
-replayed.
+Per step: one ckv_append_tokens launch writes every sequence's new key and
+value into the page slot its block table gives for the new position and
+recomputes that block's summary; then ckv_decode_step scores, selects and
+attends.  All per-step inputs (queries, new keys and values, lengths) are
+staged on the device up front and passed to the calls in place, and every
+step writes its own output buffers, so a step is exactly two launches and
+any run of steps can be captured into one HIP graph and replayed.
 """
 from __future__ import annotations
 
@@ -52,12 +51,12 @@ class DecodeLoop:
             C.allocate_workspace(C.workspace_bytes(dims, self.budget), device)
 
     def step(self, t: int) -> None:
+        """Step t: lengths self.lens[t] (they count the new token), query
+        self.q[t]; the device inputs' own q and seq_lens are not used."""
         d = self.dev
-        d.seq_lens.copy_(self.lens[t])
-        d.q.copy_(self.q[t])
         C.append_tokens(self.dims, self.k_new[t], self.v_new[t], d.k_cache, d.v_cache, d.block_table,
-                        d.seq_lens, self.summ)
-        C.decode_step(self.dims, d.q, d.k_cache, d.v_cache, self.summ, d.block_table, d.seq_lens,
+                        self.lens[t], self.summ)
+        C.decode_step(self.dims, self.q[t], d.k_cache, d.v_cache, self.summ, d.block_table, self.lens[t],
                       self.budget, self.ws, selected=self.selected[t], num_selected=self.num_selected[t],
                       out=self.out[t], lse=self.lse[t])
 
