@@ -322,7 +322,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the decode step shards by KV head or by sequence; see the design notes)",
+              "(across GPUs the decode step would shard by sequence or by KV head, one share per process)",
               file=sys.stderr, flush=True)
         return 2
 
