@@ -152,12 +152,16 @@ ckv_status ckv_append_tokens(const ckv_dims* dims, const void* k_new, const void
  * ckv_compensated_decode_attention and ckv_decode_step need for these dims
  * and this budget (0 when dims are invalid).  The same workspace must be
  * passed to both calls of one decode step.
- * The workspace must be zero-filled before its first use: its first
- * 64 + 4 * B * Hkv uint32 words are the step kernel's control words (work
- * tickets and per-(sequence, KV head) arrival counters), which every call
- * returns to zero.  Word 2 is an error flag that a call sets, and leaves
- * set, if one of its bounded waits ever ran out (results are then
- * unspecified).  Calls that share a workspace must not overlap. */
+ * The workspace must be zero-filled before its first use, and it serves one
+ * (dims, budget_tokens) pair: its layout depends on both, so zero it again
+ * before using it with other dims or another budget.  Its first
+ * 64 + 8 * B * Hkv uint32 words are control words.  Word 2 is an error flag
+ * that a call sets, and leaves set, if one of its bounded waits ever ran out
+ * (results are then unspecified).  Word 64 + 8 * (b * Hkv + g) + 3 counts
+ * the ckv_decode_step calls of sequence b, KV head g; every other control
+ * word is zero again after each call, and so is the half of the single-launch
+ * step's published words that its next call publishes into.  Calls that
+ * share a workspace must not overlap. */
 size_t ckv_workspace_bytes(const ckv_dims* dims, int32_t budget_tokens);
 
 /* Score every block and select the top-k per (sequence, KV head) under a
