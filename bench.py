@@ -225,8 +225,9 @@ def decode_loop(args, dev0) -> int:
     """Prefill plus a generation loop at 128K context (Llama-3.1-8B layer
     shape): the bulk summary build over 131072 tokens, then 64 decode steps,
     each appending one token (written into its page and the tail block's
-    summary refreshed, in one launch) and running the step with a 2048-token
-    budget.  The
+    summary refreshed) and running the step with a 2048-token budget, in one
+    ckv_decode_step_append call (with --loop-two-launch: ckv_append_tokens,
+    then ckv_decode_step).  The
     steps of all layer copies are captured into one HIP graph and replayed;
     a step visits every layer copy in turn, as a model's layer loop would, so
     summaries come from HBM."""
@@ -258,7 +259,8 @@ def decode_loop(args, dev0) -> int:
         ev[1].record()
         torch.cuda.synchronize()
         build_ms.append(ev[0].elapsed_time(ev[1]))
-        loops.append(DecodeLoop(dev, summ, w.block_table, w.seq_lens, steps, w.dtype))
+        loops.append(DecodeLoop(dev, summ, w.block_table, w.seq_lens, steps, w.dtype,
+                                fused=not args.loop_two_launch))
 
     def run_all():
         for t in range(n_steps):
@@ -282,9 +284,12 @@ def decode_loop(args, dev0) -> int:
                       "budget_tokens": w.budget_tokens, "layer_copies": n_layers,
                       "prefill_build_us": round(float(np.median(build_ms)) * 1e3, 1),
                       "us_per_layer_step": round(us, 2),
-                      "per_layer_step": "ckv_append_tokens (new key and value into their page, "
-                                        "tail-block summary), then ckv_decode_step",
-                      "launches_per_decode_step": C.decode_step_launches(dims, w.budget_tokens),
+                      "per_layer_step": ("ckv_append_tokens (new key and value into their page, "
+                                         "tail-block summary), then ckv_decode_step" if args.loop_two_launch
+                                         else "ckv_decode_step_append (append and step)"),
+                      "launches_per_layer_step": (1 + C.decode_step_launches(dims, w.budget_tokens)
+                                                  if args.loop_two_launch
+                                                  else C.decode_step_append_launches(dims, w.budget_tokens)),
                       "data": "synthetic"}), flush=True)
     return 0
 
@@ -314,6 +319,8 @@ def main() -> int:
                     help="only time the prefill summary build and a 64-step appending decode loop at 128K "
                          "context, 2048-token budget, captured into one HIP graph; one JSON line")
     ap.add_argument("--loop-layers", type=int, default=8, help="layer copies the decode loop visits per step")
+    ap.add_argument("--loop-two-launch", action="store_true",
+                    help="decode loop: append and step as two calls instead of ckv_decode_step_append")
     args = ap.parse_args()
 
     if args.rocprof_summary:

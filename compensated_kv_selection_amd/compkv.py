@@ -30,6 +30,8 @@ EXPORTS = (
     "ckv_compensated_decode_attention",
     "ckv_decode_step",
     "ckv_decode_step_launches",
+    "ckv_decode_step_append",
+    "ckv_decode_step_append_launches",
     "ckv_dense_workspace_bytes",
     "ckv_dense_decode_attention",
     "ckv_status_string",
@@ -78,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ckv_compensated_decode_attention": (I32, [D, P, P, P, S, P, P, I32, P, P, I32, P, P, P, SZ, P]),
         "ckv_decode_step": (I32, [D, P, P, P, S, P, P, I32, I32, P, P, P, P, P, SZ, P]),
         "ckv_decode_step_launches": (I32, [D, I32]),
+        "ckv_decode_step_append": (I32, [D, P, P, P, P, P, S, P, P, I32, I32, P, P, P, P, P, SZ, P]),
+        "ckv_decode_step_append_launches": (I32, [D, I32]),
         "ckv_dense_workspace_bytes": (SZ, [D]),
         "ckv_dense_decode_attention": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "ckv_status_string": (ctypes.c_char_p, [I32]),
@@ -192,6 +196,17 @@ def decode_step_launches(dims: Dims, budget_tokens: int) -> int:
     return n
 
 
+def decode_step_append_launches(dims: Dims, budget_tokens: int) -> int:
+    """Kernel launches decode_step_append makes for these dims on the current
+    device: 1 when the append runs inside the single-launch step, else the
+    append's launch plus decode_step's."""
+    d = dims.c()
+    n = int(load_library().ckv_decode_step_append_launches(ctypes.byref(d), budget_tokens))
+    if n == 0:
+        raise ValueError("invalid dims or budget")
+    return n
+
+
 def dense_workspace_bytes(dims: Dims) -> int:
     d = dims.c()
     return int(load_library().ckv_dense_workspace_bytes(ctypes.byref(d)))
@@ -278,6 +293,32 @@ def decode_step(dims: Dims, q, k_cache, v_cache, summaries: Summaries, block_tab
         ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(s), _ptr(block_table),
         _ptr(seq_lens), budget_tokens, score_mode, _ptr(selected), _ptr(num_selected), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return selected, num_selected, out, lse
+
+
+def decode_step_append(dims: Dims, q, k_new, v_new, k_cache, v_cache, summaries: Summaries, block_table,
+                       seq_lens, budget_tokens: int, workspace: torch.Tensor, score_mode: int = SCORE_COMPKV,
+                       selected=None, num_selected=None, out=None, lse=None):
+    """append_tokens followed by decode_step, as one call (one launch where
+    the library can fuse them); seq_lens already count the new token."""
+    lib = load_library()
+    dev = q.device
+    B, H = dims.batch, dims.num_kv_heads
+    kmax = dims.kmax(budget_tokens)
+    if selected is None:
+        selected = torch.empty((B, H, max(kmax, 1)), dtype=torch.int32, device=dev)
+    if num_selected is None:
+        num_selected = torch.empty((B, H), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=dev)
+    d = dims.c()
+    s = summaries.c()
+    _check(lib.ckv_decode_step_append(
+        ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), ctypes.byref(s),
+        _ptr(block_table), _ptr(seq_lens), budget_tokens, score_mode, _ptr(selected), _ptr(num_selected),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return selected, num_selected, out, lse
 
 

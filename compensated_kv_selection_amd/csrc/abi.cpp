@@ -83,6 +83,7 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.n_splits = splits;
   x.pages_per_split = x.kmax > 0 ? (x.kmax + splits - 1) / splits : 1;
   x.dtype = d->kv_dtype;
+  x.append = 0;
   x.tau = (float)(1.0 / sqrt((double)d->head_dim));
   x.tau2 = (float)(1.0 / (double)d->head_dim);
   if (G * (x.n_chunks + 2 * x.n_splits) > ckv::kMergeFactors)
@@ -231,6 +232,17 @@ bool plan_fused(ckv::Shape* s, hipStream_t stream, bool probe) {
   return true;
 }
 
+// The single launch that also appends the new tokens: bf16, d = 128, r = 4,
+// and every pair's workgroups on one XCD, so that the new token's rows and
+// the tail block's summary reach the pair's readers through that XCD's L2.
+bool plan_fused_append(ckv::Shape* s, hipStream_t stream, bool probe) {
+  if (s->dtype != CKV_BF16 || s->D != 128 || s->r != 4) return false;
+  s->append = 1;
+  if (plan_fused(s, stream, probe) && s->n_xcd > 0) return true;
+  s->append = 0;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,6 +373,46 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
   if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
   return hip_status(e, "decode step launches");
+}
+
+ckv_status ckv_decode_step_append(const ckv_dims* dims, const void* q, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache,
+                                  const ckv_summaries* summaries, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t budget_tokens, int32_t score_mode,
+                                  int32_t* selected, int32_t* num_selected, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (budget_tokens < 0) return fail(CKV_ERR_INVALID_ARG, "budget_tokens must be >= 0");
+  ckv::Shape s;
+  CKV_TRY(make_shape(dims, budget_tokens, &s));
+  if (!q || !k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "q, k_cache or v_cache is NULL");
+  if (!k_new || !v_new) return fail(CKV_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  if (!block_table || !seq_lens) return fail(CKV_ERR_INVALID_ARG, "block_table or seq_lens is NULL");
+  if (!num_selected || (!selected && s.kmax > 0))
+    return fail(CKV_ERR_INVALID_ARG, "selected or num_selected is NULL");
+  if (!out) return fail(CKV_ERR_INVALID_ARG, "out is NULL");
+  if (score_mode != CKV_SCORE_COMPKV && score_mode != CKV_SCORE_MASS)
+    return fail(CKV_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+  CKV_TRY(check_summaries(summaries));
+  CKV_TRY(check_workspace(s, workspace, workspace_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ckv::Shape sa = s;
+  if (plan_fused_append(&sa, st, true)) {
+    ckv::StepIO io{q, k_cache, v_cache, to_summ(summaries), block_table, seq_lens, selected,
+                   num_selected, nullptr, out, lse, score_mode, 1, k_new, v_new};
+    return hip_status(ckv::launch_fused(sa, io, carve(s, workspace), st), "decode step launch");
+  }
+  const hipError_t e = ckv::launch_append_tokens(s, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                                 to_summ(summaries), st);
+  if (e != hipSuccess) return hip_status(e, "append launch");
+  return ckv_decode_step(dims, q, k_cache, v_cache, summaries, block_table, seq_lens, budget_tokens,
+                         score_mode, selected, num_selected, out, lse, workspace, workspace_bytes, stream);
+}
+
+int32_t ckv_decode_step_append_launches(const ckv_dims* dims, int32_t budget_tokens) {
+  ckv::Shape s;
+  if (budget_tokens < 0 || make_shape(dims, budget_tokens, &s) != CKV_OK) return 0;
+  if (plan_fused_append(&s, nullptr, true)) return 1;
+  return 1 + (plan_fused(&s, nullptr, false) ? 1 : 3);
 }
 
 int32_t ckv_decode_step_launches(const ckv_dims* dims, int32_t budget_tokens) {

@@ -67,7 +67,7 @@ constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
 constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
 constexpr int kXccProbeBlocks = 256;       // workgroups of the XCD placement check
 
-template <int D, int G>
+template <int D, int G, bool kApp>
 struct CtlLds {
   static constexpr int CPR = D / 8;  // 16-byte pieces per mean-key row
   float qf[NT * 8];       // this KV head's query rows (G * D), then zeros
@@ -95,6 +95,10 @@ struct CtlLds {
   uint64_t tlo;           // lower bound of the pair's k-th largest candidate
   uint64_t surv[64];      // candidates at or above it
   uint32_t nown;          // selected blocks of this chunk
+  uint4 tmk[D / 8];       // decode append: the tail block's new mean key (stored bits),
+  float tgv[4];           //   its grouped variances (r = 4)
+  float tmv[D];           //   and its new mean value as stored
+  uint4 tail[kApp ? 2 * NT : 1];  // decode append: the tail page's key rows, then value rows
 };
 
 template <int D, int G>
@@ -110,9 +114,9 @@ struct MergeLds {
   float4 pa[NT];
 };
 
-template <int D, int G>
+template <int D, int G, bool kApp>
 union FusedLds {
-  CtlLds<D, G> c;
+  CtlLds<D, G, kApp> c;
   ValLds<D, G> v;
   MergeLds<D, G> m;
 };
@@ -277,9 +281,9 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
 // ---------------------------------------------------------------------------
 // Control workgroup of chunk `chunk` of pair bg.
 // ---------------------------------------------------------------------------
-template <typename KV, int D, int G, bool kR4>
+template <typename KV, int D, int G, bool kR4, bool kApp>
 __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
-                          CtlLds<D, G>& L) {
+                          CtlLds<D, G, kApp>& L) {
   constexpr int LPR = D / 8, RS = NT / LPR;
   constexpr int KT = D / 32, CPR = D / 8, RPI = 64 / CPR, NMU = CPR;  // NMU: 64 rows per wave / RPI
   constexpr bool MF = std::is_same<KV, uint16_t>::value;
@@ -301,6 +305,21 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   const int r = s.r, gs = D / r;
   const float* gv = io.summ.gvar + row0 * r;
   uint32_t* err = w.ctrl + 2;
+  // Decode append (kApp): the sequence's last token is new.  The control
+  // workgroup of the chunk holding its block (row ti of the chunk, tn tokens)
+  // writes it into its page slot and recomputes the block's summary, with
+  // the same arithmetic as the summary build; nobody reads that slot before.
+  static_assert(!kApp || (MF && kR4 && D == 128), "the appending instance is bf16, d = 128, r = 4");
+  bool app = false;
+  int tpage = -1, tn = 0, ti = 0;
+  if constexpr (kApp) {
+    if (M > 0 && chunk == (M - 1) / kChunk) {
+      tpage = ld_uniform(io.block_table + (size_t)b * s.max_blocks + M - 1);
+      app = tpage >= 0 && tpage < s.P;
+      tn = Lseq - (M - 1) * s.bs;
+      ti = M - 1 - start;
+    }
+  }
 
   // ---- loads, all issued at once, oldest first: q, page-table entries, the
   // matrix-operand rows of q, then the chunk's mean keys and variances.
@@ -351,6 +370,29 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         gvr[4 * q + 2] = v.z;
         gvr[4 * q + 3] = v.w;
       }
+    }
+  }
+  // decode append: row rs, slice c of the tail page's keys and values (16
+  // rows x 16 slices), the new token's row taken from k_new / v_new, loaded
+  // straight into LDS (thread tid's 16 bytes at L.tail[tid], values at
+  // L.tail[NT + tid]), so that no registers are held while the mean keys
+  // arrive
+  if constexpr (kApp) {
+    if (app) {
+      const KV* ks;
+      const KV* vs;
+      if (rs == tn - 1) {
+        const size_t o = ((size_t)b * s.Hkv + g) * D + c * 8;
+        ks = static_cast<const KV*>(io.k_new) + o;
+        vs = static_cast<const KV*>(io.v_new) + o;
+      } else {
+        const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
+        ks = static_cast<const KV*>(io.k_cache) + o;
+        vs = static_cast<const KV*>(io.v_cache) + o;
+      }
+      typedef __attribute__((address_space(3))) void* LdsPtr;
+      __builtin_amdgcn_global_load_lds(ks, (LdsPtr)&L.tail[64 * wave], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, (LdsPtr)&L.tail[NT + 64 * wave], 16, 0, 0);
     }
   }
   // q rows to LDS; partial |q|^2 of each thread's 8 channels
@@ -490,6 +532,103 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   __syncthreads();
 
+  // ---- decode append: the tail block's summary, stores, and its logits again ----
+  if constexpr (kApp) {
+    if (app) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have reached LDS
+      __syncthreads();
+      if (wave == 0) {
+        // lanes 0-15: key slice `lane`, 16-31: value slice lane - 16; lanes
+        // 32-63 repeat them and store nothing (the group sum takes every lane)
+        const int sl = lane & (LPR - 1);
+        const bool isv = (lane & LPR) != 0;
+        Raw8<KV> raw[kBlockSize];
+#pragma unroll
+        for (int t = 0; t < kBlockSize; ++t) raw[t].a = L.tail[(isv ? NT : 0) + t * LPR + sl];
+        float mu8[8], var[8];
+        slice_mean(raw, tn, mu8);
+        slice_sqdev(raw, tn, mu8, var);
+        float vsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsum += var[e];
+        const float gvv = group_variance_lanes(vsum, D / 4, tn);
+        uint4 wb;
+        wb.x = bf16_rne(mu8[0]) | (bf16_rne(mu8[1]) << 16);
+        wb.y = bf16_rne(mu8[2]) | (bf16_rne(mu8[3]) << 16);
+        wb.z = bf16_rne(mu8[4]) | (bf16_rne(mu8[5]) << 16);
+        wb.w = bf16_rne(mu8[6]) | (bf16_rne(mu8[7]) << 16);
+        const size_t srow = (size_t)bg * s.max_blocks + M - 1;
+        if (lane < 2 * LPR) {
+          KV* dst = static_cast<KV*>(isv ? io.summ.mean_v : io.summ.mean_k) + srow * D + sl * 8;
+          *reinterpret_cast<uint4*>(dst) = wb;
+          if (isv) {
+            float* tv = L.tmv + sl * 8;
+            tv[0] = bf16_lo(wb.x); tv[1] = bf16_hi(wb.x); tv[2] = bf16_lo(wb.y); tv[3] = bf16_hi(wb.y);
+            tv[4] = bf16_lo(wb.z); tv[5] = bf16_hi(wb.z); tv[6] = bf16_lo(wb.w); tv[7] = bf16_hi(wb.w);
+          } else {
+            L.tmk[sl] = wb;
+            if (sl % 4 == 0) {
+              io.summ.gvar[srow * 4 + sl / 4] = gvv;
+              L.tgv[sl / 4] = gvv;
+            }
+          }
+        }
+        if (lane == 0 && g == 0) io.summ.count[(size_t)b * s.max_blocks + M - 1] = tn;
+      }
+      if (rs == tn - 1) {  // the new token into its page slot
+        const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
+        *reinterpret_cast<uint4*>(static_cast<KV*>(const_cast<void*>(io.k_cache)) + o) = L.tail[tid];
+        *reinterpret_cast<uint4*>(static_cast<KV*>(const_cast<void*>(io.v_cache)) + o) = L.tail[NT + tid];
+      }
+      __syncthreads();
+      if (need_mu && wave == ti / 64) {
+        // the tail row's block-mean logits and variance estimates again, on
+        // the same matrix-core path (other rows of the tile are not used)
+        const int rr = ti % 16;
+        uint4* st = L.u.stage[wave];
+        if (lane < CPR) st[rr * CPR + (lane ^ (rr & (CPR - 1)))] = L.tmk[lane];
+        __builtin_amdgcn_wave_barrier();
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          // this lane's q operand again, from the float copy in LDS (exact
+          // bf16 values; zeros past G), as the loads gave it
+          const float* qp = L.qf + (lane & 15) * D + 32 * kt + 8 * (lane >> 4);
+          uint4 qw;
+          qw.x = (__float_as_uint(qp[0]) >> 16) | (__float_as_uint(qp[1]) & 0xffff0000u);
+          qw.y = (__float_as_uint(qp[2]) >> 16) | (__float_as_uint(qp[3]) & 0xffff0000u);
+          qw.z = (__float_as_uint(qp[4]) >> 16) | (__float_as_uint(qp[5]) & 0xffff0000u);
+          qw.w = (__float_as_uint(qp[6]) >> 16) | (__float_as_uint(qp[7]) & 0xffff0000u);
+          const int r2 = lane & 15, ch = 4 * kt + (lane >> 4);
+          const uint4 bv = st[r2 * CPR + (ch ^ (r2 & (CPR - 1)))];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qw), __builtin_bit_cast(bf16x8_t, bv),
+                                                        acc, 0, 0, 0);
+        }
+        if ((lane & 15) == rr && holder) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 4 * (lane >> 4) + i;
+            if (j < G) {
+              L.sb[j][ti] = acc[i] * s.tau;
+              float sig = 0.f;
+              if (ranked) {
+                sig = fmaf(L.qn[j * 4 + 0], L.tgv[0], sig);
+                sig = fmaf(L.qn[j * 4 + 1], L.tgv[1], sig);
+                sig = fmaf(L.qn[j * 4 + 2], L.tgv[2], sig);
+                sig = fmaf(L.qn[j * 4 + 3], L.tgv[3], sig);
+              }
+              L.lam[j][ti] = sig * s.tau2;
+            }
+          }
+        }
+      }
+      // the stores above are in L2 before the weights go out: the value
+      // workgroup reads the new mean value row only after them
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
   // ---- per head: chunk max, Z_hat part, compensation weights, log-scores ----
   if (need_mu) {
     const Coh hdr(hdr_half(s, w, tag) + (size_t)bg * s.n_chunks * G, (size_t)s.n_chunks * G * 8, s.n_xcd > 0);
@@ -554,6 +693,11 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (lam != -INFINITY && lz != -INFINITY) S += expf(lam - lz);
       }
       mykey = fused_key(S, start + tid, L.pgt[tid]);
+    }
+    // decode append: the new token's rows are in L2 before any candidate
+    // that leads another workgroup to them is published
+    if constexpr (kApp) {
+      if (app) __builtin_amdgcn_s_waitcnt(0);
     }
     // the chunk's top-k candidates, published largest first
     const Coh cand(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8,
@@ -698,6 +842,9 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     n_gather = nrows;
     L.gblk[tid] = start + tid;
     L.gpg[tid] = L.pgt[tid];
+    if constexpr (kApp) {
+      if (app) __builtin_amdgcn_s_waitcnt(0);  // the new token's rows, read back below
+    }
     __syncthreads();
   }
 
@@ -750,6 +897,12 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           const int ri = L.own[e];
           float nv[8];
           load8(mv + (size_t)ri * D + c * 8, nv);
+          if constexpr (kApp) {
+            if (app && ri == ti) {
+#pragma unroll
+              for (int e2 = 0; e2 < 8; ++e2) nv[e2] = L.tmv[c * 8 + e2];
+            }
+          }
 #pragma unroll
           for (int j = 0; j < G; ++j) {
             const float wt = L.wt[j][ri];
@@ -839,8 +992,6 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   if (comp) {
     const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8, s.n_xcd > 0);
     uint32_t spins = 0;
-    // the chunk maxima come last from the control workgroup: once they are
-    // here, its mean keys have arrived and the mean values may stream
     if (tid < G) L.mx[tid] = read_tagged(wts, tid * kWStride + kChunk, wts.u64(tid * kWStride + kChunk), tag, spins, err);
     __syncthreads();
     // this thread's weights: row tid of every head, all requested together
@@ -988,9 +1139,9 @@ __device__ __forceinline__ void warm_kernel_args() {
   asm volatile("" ::"s"(x));
 }
 
-template <typename KV, int D, int G, bool kR4>
+template <typename KV, int D, int G, bool kR4, bool kApp>
 __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
-  __shared__ FusedLds<D, G> lds;
+  __shared__ FusedLds<D, G, kApp> lds;
   warm_kernel_args();
   // This workgroup's pair (of the round) and role: control workgroup of
   // chunk `role` (role < n_chunks), else value workgroup role - n_chunks.
@@ -1018,7 +1169,7 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
   for (int bg = pair; bg < s.B * s.Hkv; bg += s.bg_round) {
     const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
     if (role < s.n_chunks) {
-      ctl_chunk<KV, D, G, kR4>(s, io, w, bg, role, epoch + 1u, lds.c);
+      ctl_chunk<KV, D, G, kR4, kApp>(s, io, w, bg, role, epoch + 1u, lds.c);
       __syncthreads();
       merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m);
     } else {
@@ -1043,26 +1194,28 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
 }
 
 // Calls f(kernel, index) with the fused kernel instance for (dtype, D, G,
-// r == 4); index < 32.  bf16 has a separate instance for r == 4, which keeps
-// the variances of the rows of its matrix-core results in registers; f32
-// scores on the vector ALU and reads them from memory whatever r is.
+// r == 4, append); index < 32.  bf16 has a separate instance for r == 4,
+// which keeps the variances of the rows of its matrix-core results in
+// registers; f32 scores on the vector ALU and reads them from memory
+// whatever r is.  The appending instances exist for bf16, D = 128, r = 4.
 template <class F>
 auto with_fused(const Shape& s, F&& f) {
-#define CKV_G(KV, DD, R4, I)                                           \
-  switch (s.G) {                                                       \
-    case 1: return f(&fused_step_kernel<KV, DD, 1, R4>, (I) + 0);      \
-    case 2: return f(&fused_step_kernel<KV, DD, 2, R4>, (I) + 1);      \
-    case 4: return f(&fused_step_kernel<KV, DD, 4, R4>, (I) + 2);      \
-    default: return f(&fused_step_kernel<KV, DD, 8, R4>, (I) + 3);     \
+#define CKV_G(KV, DD, R4, I, APP)                                           \
+  switch (s.G) {                                                            \
+    case 1: return f(&fused_step_kernel<KV, DD, 1, R4, APP>, (I) + 0);      \
+    case 2: return f(&fused_step_kernel<KV, DD, 2, R4, APP>, (I) + 1);      \
+    case 4: return f(&fused_step_kernel<KV, DD, 4, R4, APP>, (I) + 2);      \
+    default: return f(&fused_step_kernel<KV, DD, 8, R4, APP>, (I) + 3);     \
   }
+  if (s.append) { CKV_G(uint16_t, 128, true, 24, true) }
   if (s.dtype == 0) {
     if (s.r == 4) {
-      if (s.D == 128) { CKV_G(uint16_t, 128, true, 0) } else { CKV_G(uint16_t, 64, true, 4) }
+      if (s.D == 128) { CKV_G(uint16_t, 128, true, 0, false) } else { CKV_G(uint16_t, 64, true, 4, false) }
     } else {
-      if (s.D == 128) { CKV_G(uint16_t, 128, false, 8) } else { CKV_G(uint16_t, 64, false, 12) }
+      if (s.D == 128) { CKV_G(uint16_t, 128, false, 8, false) } else { CKV_G(uint16_t, 64, false, 12, false) }
     }
   } else {
-    if (s.D == 128) { CKV_G(float, 128, true, 16) } else { CKV_G(float, 64, true, 20) }
+    if (s.D == 128) { CKV_G(float, 128, true, 16, false) } else { CKV_G(float, 64, true, 20, false) }
   }
 #undef CKV_G
 }

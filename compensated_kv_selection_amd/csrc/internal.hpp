@@ -53,6 +53,8 @@ struct Shape {
   int dtype;          // 0 = bf16, 1 = f32
   float tau;          // 1 / sqrt(d)
   float tau2;         // 1 / d
+  int append;         // fused, host side: 1 = the instance that also appends each sequence's
+                      //   new token (StepIO k_new, v_new)
 };
 
 // Device pointers carved from the caller's workspace.
@@ -95,6 +97,10 @@ struct StepIO {
   float* lse;
   int score_mode;
   int compensate;
+  // Fused step with append only: the new key and value rows, [B][Hkv][D];
+  // k_cache, v_cache and the summaries are then written.
+  const void* k_new;
+  const void* v_new;
 };
 
 hipError_t launch_build_summaries(const Shape& s, const void* k_cache, const void* v_cache,

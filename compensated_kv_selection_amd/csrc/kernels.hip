@@ -92,40 +92,15 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
       for (int t = 0; t < kBlockSize; ++t)
         if (t == n - 1) raw[t] = nr;
     }
-    float x0[8], sx[8], x[8];
-    raw_float(raw[0], x0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sx[e] = 0.f;
-#pragma unroll
-    for (int t = 1; t < kBlockSize; ++t) {
-      if (t < n) {
-        raw_float(raw[t], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sx[e] += x[e] - x0[e];
-      }
-    }
     float mu[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mu[e] = x0[e] + sx[e] / fn;
+    slice_mean(raw, n, mu);
     const size_t row = (((size_t)b * s.Hkv + g) * s.max_blocks + i) * D + c * 8;
-    float vs = 0.f;  // keys: the slice's channel variances summed
+    float vs = 0.f;  // keys: the slice's squared deviations summed
     if (isv) {
       store8(mv + row, mu);
     } else {
       float var[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) var[e] = 0.f;
-#pragma unroll
-      for (int t = 0; t < kBlockSize; ++t) {  // second pass: population variance
-        if (t < n) {
-          raw_float(raw[t], x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float dl = x[e] - mu[e];
-            var[e] = fmaf(dl, dl, var[e]);
-          }
-        }
-      }
+      slice_sqdev(raw, n, mu, var);
       if (lanes_sum) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vs += var[e];
@@ -138,14 +113,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
     if (lanes_sum) {
       // the group's slices are adjacent lanes of one row (gs / 8 of them,
       // aligned): sum them across lanes
-      const int wl = gs / 8;
-      float gsum = vs;
-      if (wl > 1) gsum += __uint_as_float(lane_xor<1>(__float_as_uint(gsum)));
-      if (wl > 2) gsum += __uint_as_float(lane_xor<2>(__float_as_uint(gsum)));
-      if (wl > 4) gsum += __uint_as_float(lane_xor<4>(__float_as_uint(gsum)));
-      if (wl > 8) gsum += __uint_as_float(lane_xor<8>(__float_as_uint(gsum)));
-      if (!isv && c % wl == 0)
-        gv[(((size_t)b * s.Hkv + g) * s.max_blocks + i) * s.r + c / wl] = gsum / (fn * (float)gs);
+      const float gvv = group_variance_lanes(vs, gs, n);
+      if (!isv && c % (gs / 8) == 0) gv[(((size_t)b * s.Hkv + g) * s.max_blocks + i) * s.r + c / (gs / 8)] = gvv;
     }
   }
   if (!lanes_sum) {

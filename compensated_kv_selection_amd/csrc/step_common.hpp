@@ -359,6 +359,60 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
   }
 }
 
+// ---- one block's summary, per 8-channel slice (shared by the summary build
+// and the single-launch step's decode append, so both give the same bits) ----
+// Mean of rows 0..n-1 of a 16-row block, accumulated on data shifted by row
+// 0 (a block of equal rows gets exactly that row as mean).
+template <typename KV>
+__device__ __forceinline__ void slice_mean(const Raw8<KV> (&raw)[kBlockSize], int n, float (&mu)[8]) {
+  float x0[8], sx[8], x[8];
+  raw_float(raw[0], x0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sx[e] = 0.f;
+#pragma unroll
+  for (int t = 1; t < kBlockSize; ++t) {
+    if (t < n) {
+      raw_float(raw[t], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sx[e] += x[e] - x0[e];
+    }
+  }
+  const float fn = (float)n;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = x0[e] + sx[e] / fn;
+}
+// Sum over rows 0..n-1 of the squared deviations from mu (second pass).
+template <typename KV>
+__device__ __forceinline__ void slice_sqdev(const Raw8<KV> (&raw)[kBlockSize], int n, const float (&mu)[8],
+                                            float (&var)[8]) {
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) var[e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < kBlockSize; ++t) {
+    if (t < n) {
+      raw_float(raw[t], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float dl = x[e] - mu[e];
+        var[e] = fmaf(dl, dl, var[e]);
+      }
+    }
+  }
+}
+// The grouped variance of a group of gs channels that spans wl = gs / 8
+// adjacent, aligned lanes (each lane passing the sum of its slice's squared
+// deviations): the sum across the group's lanes over n * gs.
+__device__ __forceinline__ float group_variance_lanes(float vs, int gs, int n) {
+  const int wl = gs / 8;
+  float gsum = vs;
+  if (wl > 1) gsum += __uint_as_float(lane_xor<1>(__float_as_uint(gsum)));
+  if (wl > 2) gsum += __uint_as_float(lane_xor<2>(__float_as_uint(gsum)));
+  if (wl > 4) gsum += __uint_as_float(lane_xor<4>(__float_as_uint(gsum)));
+  if (wl > 8) gsum += __uint_as_float(lane_xor<8>(__float_as_uint(gsum)));
+  return gsum / ((float)n * (float)gs);
+}
+
 // Compare-exchange with lane ^ J: this lane keeps the larger key if
 // keep_max, else the smaller.
 template <int J>

@@ -1,13 +1,15 @@
 """A generation loop over one paged attention layer: every step appends one
 token per sequence and runs the compensated decode step on the grown context.
 
-Per step: one ckv_append_tokens launch writes every sequence's new key and
-value into the page slot its block table gives for the new position and
-recomputes that block's summary; then ckv_decode_step scores, selects and
-attends.  All per-step inputs (queries, new keys and values, lengths) are
-staged on the device up front and passed to the calls in place, and every
-step writes its own output buffers, so a step is exactly two launches and
-any run of steps can be captured into one HIP graph and replayed.
+Per step, one ckv_decode_step_append call writes every sequence's new key
+and value into the page slot its block table gives for the new position,
+recomputes that block's summary, then scores, selects and attends.  Where
+the library fuses the two that is one launch; otherwise (and with
+``fused=False``) it is ckv_append_tokens followed by ckv_decode_step.  All
+per-step inputs (queries, new keys and values, lengths) are staged on the
+device up front and passed to the calls in place, and every step writes its
+own output buffers, so any run of steps can be captured into one HIP graph
+and replayed.
 """
 from __future__ import annotations
 
@@ -22,14 +24,15 @@ from .tensors import DeviceInputs, storage_to_torch
 
 class DecodeLoop:
     def __init__(self, dev: DeviceInputs, summaries: C.Summaries, block_table: np.ndarray,
-                 start_lens: Sequence[int], steps, dtype: str, workspace: torch.Tensor = None):
+                 start_lens: Sequence[int], steps, dtype: str, workspace: torch.Tensor = None,
+                 fused: bool = True):
         """``steps`` holds per-step ``q`` [B, Hq, d], ``k_new`` and ``v_new``
         [B, Hkv, d] in storage form; ``start_lens`` are the lengths before the
         first step.  Raises if a sequence runs out of pages."""
         dims = dev.dims
         device = dev.q.device
         B, T, bs = dims.batch, len(steps), dims.block_size
-        self.dev, self.summ, self.dims, self.T = dev, summaries, dims, T
+        self.dev, self.summ, self.dims, self.T, self.fused = dev, summaries, dims, T, fused
         self.budget = dev.budget_tokens
         lens = np.zeros((T, B), dtype=np.int32)
         for t in range(T):
@@ -54,6 +57,12 @@ class DecodeLoop:
         """Step t: lengths self.lens[t] (they count the new token), query
         self.q[t]; the device inputs' own q and seq_lens are not used."""
         d = self.dev
+        if self.fused:
+            C.decode_step_append(self.dims, self.q[t], self.k_new[t], self.v_new[t], d.k_cache, d.v_cache,
+                                 self.summ, d.block_table, self.lens[t], self.budget, self.ws,
+                                 selected=self.selected[t], num_selected=self.num_selected[t],
+                                 out=self.out[t], lse=self.lse[t])
+            return
         C.append_tokens(self.dims, self.k_new[t], self.v_new[t], d.k_cache, d.v_cache, d.block_table,
                         self.lens[t], self.summ)
         C.decode_step(self.dims, self.q[t], d.k_cache, d.v_cache, self.summ, d.block_table, self.lens[t],

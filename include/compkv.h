@@ -224,6 +224,35 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
  * occupancy on it (3 when no device is present); launches nothing. */
 int32_t ckv_decode_step_launches(const ckv_dims* dims, int32_t budget_tokens);
 
+/* One decode step that first appends the new token of every sequence
+ * (review FAQ: summaries are kept current as tokens enter the cache), then
+ * scores, selects and attends as ckv_decode_step.  Same results, bit for
+ * bit, as ckv_append_tokens(dims, k_new, v_new, k_cache, v_cache,
+ * block_table, seq_lens, summaries) followed by ckv_decode_step with the
+ * remaining arguments: seq_lens already count the new token, k_new and
+ * v_new are [B][Hkv][d] in kv_dtype, and k_cache, v_cache and the summaries
+ * are written.  With bf16, d = 128, r_groups = 4, and when the single-launch
+ * step applies and the device keeps each (sequence, KV head) pair's
+ * workgroups on one XCD, it is one launch: the workgroup that scores the
+ * tail block also writes the new token into its page and recomputes that
+ * block's summary.  Otherwise it makes exactly those calls.
+ * k_new and v_new must not overlap the caches or the summaries; the caller
+ * owns every buffer.  Errors: as ckv_decode_step, plus CKV_ERR_INVALID_ARG
+ * for a NULL k_new or v_new. */
+ckv_status ckv_decode_step_append(const ckv_dims* dims, const void* q, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache,
+                                  const ckv_summaries* summaries, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t budget_tokens,
+                                  int32_t score_mode, int32_t* selected, int32_t* num_selected,
+                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Number of kernel launches ckv_decode_step_append makes for these dims and
+ * budget on the current device (0 if the arguments are invalid).  The first
+ * call on a device may run the one-time XCD placement check (a small kernel
+ * on the null stream, waited for). */
+int32_t ckv_decode_step_append_launches(const ckv_dims* dims, int32_t budget_tokens);
+
 /* Dense decode attention over every token (the baseline the method is
  * measured against: review "Summary", speed-up over full attention).
  * Workspace from ckv_dense_workspace_bytes, zero-filled before first use

@@ -272,10 +272,13 @@ def test_batched_ragged():
     full_check(W.make_preset("batched_ragged", seed=0), fused=True)
 
 
-def test_prefill_then_decode_loop():
+@pytest.mark.parametrize("fused_append", [False, True])
+def test_prefill_then_decode_loop(fused_append):
     # Bulk summaries over 128K tokens, then 64 decode steps that each append one
     # token (tail-block summary update) and run the compensated step with a
-    # 2048-token budget; checked against the oracle at several steps.
+    # 2048-token budget; checked against the oracle at several steps.  The
+    # append is a write plus the append-mode summary build, or it runs inside
+    # the step (ckv_decode_step_append).
     w = W.make_preset("prefill_128k_loop", seed=0)
     steps = W.make_append_steps(w, 64, seed=21)
     kc, vc = w.paged_cache()
@@ -293,17 +296,27 @@ def test_prefill_then_decode_loop():
     osumm = O.build_summaries(k64[:L0], v64[:L0], 16, 4, "bf16")
     ws = C.allocate_workspace(C.workspace_bytes(dims, w.budget_tokens), "cuda:0")
     checkpoints = {0, 1, 15, 16, 63}
+    print(f"[case] decode loop fused_append={fused_append} launches per step "
+          f"{C.decode_step_append_launches(dims, w.budget_tokens) if fused_append else 'append + step'}",
+          flush=True)
     for t, st in enumerate(steps):
         L = L0 + t
-        p, slot = int(w.block_table[0, L // 16]), L % 16
-        dev.k_cache[p, :, slot, :] = torch.from_numpy(st.k_new[0].view(np.int16)).view(torch.bfloat16).cuda()
-        dev.v_cache[p, :, slot, :] = torch.from_numpy(st.v_new[0].view(np.int16)).view(torch.bfloat16).cuda()
+        kn = torch.from_numpy(st.k_new[0].view(np.int16)).view(torch.bfloat16).cuda()
+        vn = torch.from_numpy(st.v_new[0].view(np.int16)).view(torch.bfloat16).cuda()
         dev.seq_lens.fill_(L + 1)
         dev.q.copy_(torch.from_numpy(st.q.view(np.int16)).view(torch.bfloat16))
-        C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ,
-                          append_only=True)
-        sel, nsel, out, lse = C.decode_step(dims, dev.q, dev.k_cache, dev.v_cache, summ, dev.block_table,
-                                            dev.seq_lens, w.budget_tokens, ws)
+        if fused_append:
+            sel, nsel, out, lse = C.decode_step_append(dims, dev.q, kn.unsqueeze(0), vn.unsqueeze(0), dev.k_cache,
+                                                       dev.v_cache, summ, dev.block_table, dev.seq_lens,
+                                                       w.budget_tokens, ws)
+        else:
+            p, slot = int(w.block_table[0, L // 16]), L % 16
+            dev.k_cache[p, :, slot, :] = kn
+            dev.v_cache[p, :, slot, :] = vn
+            C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ,
+                              append_only=True)
+            sel, nsel, out, lse = C.decode_step(dims, dev.q, dev.k_cache, dev.v_cache, summ, dev.block_table,
+                                                dev.seq_lens, w.budget_tokens, ws)
         k64[L] = O.widen(st.k_new[0], "bf16")
         v64[L] = O.widen(st.v_new[0], "bf16")
         osumm = O.append_summaries(osumm, k64[:L + 1], v64[:L + 1], 16, 4, "bf16")
@@ -364,6 +377,90 @@ def test_decode_loop_graph_replays_match_eager():
         for name, x, r in zip(("out", "lse", "num_selected", "selected"), outs, ref):
             assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager loop"
         check_workspace_clean(loop.ws, dims, w.budget_tokens)
+
+
+def _append_step_case(before, num_kv_heads, budget, seed, hot, steps=3):
+    """Inputs for `steps` appending decode steps: sequences of lengths
+    `before` get one new token per step.  For sequences listed in `hot` the
+    new keys point along the mean query of their KV head, with alternating
+    sign and a large norm, so that the tail block (new tokens of very
+    different logits) is selected and attended to from the page slots the
+    steps just wrote."""
+    G = 4
+    w = W.make_decode_inputs(name="append_step", seq_lens=[max(L, 1) for L in before], num_q_heads=G * num_kv_heads,
+                             num_kv_heads=num_kv_heads, head_dim=128, r_groups=4, budget_tokens=budget,
+                             dtype="bf16", n_needles=0, n_outliers=2, extra_capacity_tokens=48, seed=seed)
+    dev = to_device(w)
+    rng = np.random.default_rng(seed + 100)
+    B, H = len(before), num_kv_heads
+    qf = dev.q.float().view(B, H, G, 128).mean(dim=2).cpu().numpy()
+    qf = qf / np.linalg.norm(qf, axis=-1, keepdims=True) * np.sqrt(128)
+    kv = []
+    for t in range(steps):
+        k_new = rng.standard_normal((B, H, 128), dtype=np.float32)
+        v_new = rng.standard_normal((B, H, 128), dtype=np.float32)
+        for b in hot:
+            k_new[b] = (6.0 if t % 2 == 0 else -6.0) * qf[b]
+        kv.append((torch.from_numpy(k_new).to("cuda:0", torch.bfloat16),
+                   torch.from_numpy(v_new).to("cuda:0", torch.bfloat16)))
+    return w, dev, kv
+
+
+@pytest.mark.parametrize("before,num_kv_heads,budget,hot", [
+    # tails at slots 8, 0, 15, 1, 0 and 15 of their blocks (the fourth and
+    # sixth sequences have every block selected), and one of length 0
+    ([1000, 768, 15, 1, 4096, 31, 0], 2, 64, [0, 1, 4]),
+    # one long sequence: 8 chunks per pair, the tail block's reader is
+    # another chunk's workgroup
+    ([32767], 8, 512, [0]),
+    ([32768 + 5], 8, 512, []),
+])
+def test_decode_step_append_matches_append_then_step(before, num_kv_heads, budget, hot):
+    # ckv_decode_step_append against ckv_append_tokens + ckv_decode_step, from
+    # the same state: outputs, selections, caches and summaries bit for bit,
+    # over three steps in a row (each appending one more token).
+    w, dev, kv = _append_step_case(before, num_kv_heads, budget, seed=41, hot=hot)
+    dims = dev.dims
+    summ = C.allocate_summaries(dims, "cuda:0")
+    C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
+    print(f"[case] decode_step_append lens={before} Hkv={num_kv_heads} budget={budget} "
+          f"launches={C.decode_step_append_launches(dims, budget)}", flush=True)
+    assert C.decode_step_append_launches(dims, budget) == 1
+
+    def state():
+        return (dev.k_cache.clone(), dev.v_cache.clone(),
+                C.Summaries(summ.mean_k.clone(), summ.mean_v.clone(), summ.gvar.clone(), summ.count.clone()))
+
+    def bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+    ka, va, sa = state()
+    kb, vb, sb = state()
+    wsa = C.allocate_workspace(C.workspace_bytes(dims, budget), "cuda:0")
+    wsb = C.allocate_workspace(C.workspace_bytes(dims, budget), "cuda:0")
+    for step, (k_new, v_new) in enumerate(kv):
+        lens = torch.tensor([L + step + 1 if L > 0 else 0 for L in before], dtype=torch.int32, device="cuda:0")
+        print(f"[case] step {step}: lens={lens.tolist()[:8]}", flush=True)
+        C.append_tokens(dims, k_new, v_new, ka, va, dev.block_table, lens, sa)
+        ra = C.decode_step(dims, dev.q, ka, va, sa, dev.block_table, lens, budget, wsa)
+        rb = C.decode_step_append(dims, dev.q, k_new, v_new, kb, vb, sb, dev.block_table, lens, budget, wsb)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("selected", "num_selected", "out", "lse"), ra, rb):
+            if name == "selected":
+                kk = ra[1].unsqueeze(-1)
+                ar = torch.arange(x.shape[-1], device=x.device)
+                x, y = x.masked_fill(ar >= kk, -1), y.masked_fill(ar >= kk, -1)
+            assert torch.equal(bits(x), bits(y)), f"step {step}: {name} differs"
+        assert torch.equal(bits(ka), bits(kb)) and torch.equal(bits(va), bits(vb)), f"step {step}: caches differ"
+        for name, x, y in zip(("mean_k", "mean_v", "gvar", "count"), (sa.mean_k, sa.mean_v, sa.gvar, sa.count),
+                              (sb.mean_k, sb.mean_v, sb.gvar, sb.count)):
+            assert torch.equal(bits(x), bits(y)), f"step {step}: summary {name} differs"
+        check_workspace_clean(wsb, dims, budget)
+    # the hot sequences did attend to their tail block
+    for b in hot:
+        L = int(lens[b])
+        for g in range(num_kv_heads):
+            assert int((L - 1) // 16) in ra[0][b, g, : int(ra[1][b, g])].tolist(), (b, g)
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
