@@ -67,7 +67,7 @@ constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
 constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
 constexpr int kXccProbeBlocks = 256;       // workgroups of the XCD placement check
 
-template <int D, int G, bool kApp>
+template <int D, int G>
 struct CtlLds {
   static constexpr int CPR = D / 8;  // 16-byte pieces per mean-key row
   float qf[NT * 8];       // this KV head's query rows (G * D), then zeros
@@ -98,7 +98,6 @@ struct CtlLds {
   uint4 tmk[D / 8];       // decode append: the tail block's new mean key (stored bits),
   float tgv[4];           //   its grouped variances (r = 4)
   float tmv[D];           //   and its new mean value as stored
-  uint4 tail[kApp ? 2 * NT : 1];  // decode append: the tail page's key rows, then value rows
 };
 
 template <int D, int G>
@@ -114,9 +113,9 @@ struct MergeLds {
   float4 pa[NT];
 };
 
-template <int D, int G, bool kApp>
+template <int D, int G>
 union FusedLds {
-  CtlLds<D, G, kApp> c;
+  CtlLds<D, G> c;
   ValLds<D, G> v;
   MergeLds<D, G> m;
 };
@@ -283,7 +282,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
 // ---------------------------------------------------------------------------
 template <typename KV, int D, int G, bool kR4, bool kApp>
 __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
-                          CtlLds<D, G, kApp>& L) {
+                          CtlLds<D, G>& L) {
   constexpr int LPR = D / 8, RS = NT / LPR;
   constexpr int KT = D / 32, CPR = D / 8, RPI = 64 / CPR, NMU = CPR;  // NMU: 64 rows per wave / RPI
   constexpr bool MF = std::is_same<KV, uint16_t>::value;
@@ -372,29 +371,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       }
     }
   }
-  // decode append: row rs, slice c of the tail page's keys and values (16
-  // rows x 16 slices), the new token's row taken from k_new / v_new, loaded
-  // straight into LDS (thread tid's 16 bytes at L.tail[tid], values at
-  // L.tail[NT + tid]), so that no registers are held while the mean keys
-  // arrive
-  if constexpr (kApp) {
-    if (app) {
-      const KV* ks;
-      const KV* vs;
-      if (rs == tn - 1) {
-        const size_t o = ((size_t)b * s.Hkv + g) * D + c * 8;
-        ks = static_cast<const KV*>(io.k_new) + o;
-        vs = static_cast<const KV*>(io.v_new) + o;
-      } else {
-        const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
-        ks = static_cast<const KV*>(io.k_cache) + o;
-        vs = static_cast<const KV*>(io.v_cache) + o;
-      }
-      typedef __attribute__((address_space(3))) void* LdsPtr;
-      __builtin_amdgcn_global_load_lds(ks, (LdsPtr)&L.tail[64 * wave], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs, (LdsPtr)&L.tail[NT + 64 * wave], 16, 0, 0);
-    }
-  }
   // q rows to LDS; partial |q|^2 of each thread's 8 channels
   {
     float x[8];
@@ -425,6 +401,27 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     L.qn[item] = a;
   }
   __syncthreads();
+  // decode append: row rs, slice c of the tail page's keys and values (16
+  // rows x 16 slices), the new token's row taken from k_new / v_new (the
+  // page slot it goes to is never read)
+  Raw8<KV> tkr, tvr;
+  if constexpr (kApp) {
+    if (app) {
+      const KV* ks;
+      const KV* vs;
+      if (rs == tn - 1) {
+        const size_t o = ((size_t)b * s.Hkv + g) * D + c * 8;
+        ks = static_cast<const KV*>(io.k_new) + o;
+        vs = static_cast<const KV*>(io.v_new) + o;
+      } else {
+        const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
+        ks = static_cast<const KV*>(io.k_cache) + o;
+        vs = static_cast<const KV*>(io.v_cache) + o;
+      }
+      raw_load(ks, tkr);
+      raw_load(vs, tvr);
+    }
+  }
 
   // ---- block-mean logits and variance estimates ----
   if (need_mu) {
@@ -535,50 +532,71 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   // ---- decode append: the tail block's summary, stores, and its logits again ----
   if constexpr (kApp) {
     if (app) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have reached LDS
-      __syncthreads();
-      if (wave == 0) {
-        // lanes 0-15: key slice `lane`, 16-31: value slice lane - 16; lanes
-        // 32-63 repeat them and store nothing (the group sum takes every lane)
-        const int sl = lane & (LPR - 1);
-        const bool isv = (lane & LPR) != 0;
-        Raw8<KV> raw[kBlockSize];
-#pragma unroll
-        for (int t = 0; t < kBlockSize; ++t) raw[t].a = L.tail[(isv ? NT : 0) + t * LPR + sl];
-        float mu8[8], var[8];
-        slice_mean(raw, tn, mu8);
-        slice_sqdev(raw, tn, mu8, var);
-        float vsum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vsum += var[e];
-        const float gvv = group_variance_lanes(vsum, D / 4, tn);
-        uint4 wb;
-        wb.x = bf16_rne(mu8[0]) | (bf16_rne(mu8[1]) << 16);
-        wb.y = bf16_rne(mu8[2]) | (bf16_rne(mu8[3]) << 16);
-        wb.z = bf16_rne(mu8[4]) | (bf16_rne(mu8[5]) << 16);
-        wb.w = bf16_rne(mu8[6]) | (bf16_rne(mu8[7]) << 16);
-        const size_t srow = (size_t)bg * s.max_blocks + M - 1;
-        if (lane < 2 * LPR) {
-          KV* dst = static_cast<KV*>(isv ? io.summ.mean_v : io.summ.mean_k) + srow * D + sl * 8;
-          *reinterpret_cast<uint4*>(dst) = wb;
-          if (isv) {
-            float* tv = L.tmv + sl * 8;
-            tv[0] = bf16_lo(wb.x); tv[1] = bf16_hi(wb.x); tv[2] = bf16_lo(wb.y); tv[3] = bf16_hi(wb.y);
-            tv[4] = bf16_lo(wb.z); tv[5] = bf16_hi(wb.z); tv[6] = bf16_lo(wb.w); tv[7] = bf16_hi(wb.w);
-          } else {
-            L.tmk[sl] = wb;
-            if (sl % 4 == 0) {
-              io.summ.gvar[srow * 4 + sl / 4] = gvv;
-              L.tgv[sl / 4] = gvv;
-            }
-          }
-        }
-        if (lane == 0 && g == 0) io.summ.count[(size_t)b * s.max_blocks + M - 1] = tn;
-      }
+      L.u.stage[0][tid] = tkr.a;  // row rs, slice c: row-major, channels in order
+      L.u.stage[1][tid] = tvr.a;
       if (rs == tn - 1) {  // the new token into its page slot
         const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
-        *reinterpret_cast<uint4*>(static_cast<KV*>(const_cast<void*>(io.k_cache)) + o) = L.tail[tid];
-        *reinterpret_cast<uint4*>(static_cast<KV*>(const_cast<void*>(io.v_cache)) + o) = L.tail[NT + tid];
+        raw_store(static_cast<KV*>(const_cast<void*>(io.k_cache)) + o, tkr);
+        raw_store(static_cast<KV*>(const_cast<void*>(io.v_cache)) + o, tvr);
+      }
+      __syncthreads();
+      // one channel per thread (keys, then values), each with the summary
+      // build's arithmetic and order for that channel
+      float* tvar = reinterpret_cast<float*>(L.u.stage[2]);  // per-channel key sums of squares
+      {
+        const bool isv = tid >= D;
+        const int ch = tid & (D - 1);
+        const uint16_t* rows = reinterpret_cast<const uint16_t*>(L.u.stage[isv ? 1 : 0]) + ch;
+        const float x0 = __uint_as_float((uint32_t)rows[0] << 16);
+        float sx = 0.f;
+#pragma unroll
+        for (int t = 1; t < kBlockSize; ++t)
+          if (t < tn) sx += __uint_as_float((uint32_t)rows[t * D] << 16) - x0;
+        const float mu = x0 + sx / (float)tn;
+        const uint32_t mb = bf16_rne(mu);
+        if (isv) {
+          L.tmv[ch] = __uint_as_float(mb << 16);
+        } else {
+          reinterpret_cast<uint16_t*>(L.tmk)[ch] = (uint16_t)mb;
+          float var = 0.f;
+#pragma unroll
+          for (int t = 0; t < kBlockSize; ++t) {
+            if (t < tn) {
+              const float dl = __uint_as_float((uint32_t)rows[t * D] << 16) - mu;
+              var = fmaf(dl, dl, var);
+            }
+          }
+          tvar[ch] = var;
+        }
+      }
+      __syncthreads();
+      const size_t srow = (size_t)bg * s.max_blocks + M - 1;
+      if (tid < LPR) {
+        *reinterpret_cast<uint4*>(static_cast<KV*>(io.summ.mean_k) + srow * D + tid * 8) = L.tmk[tid];
+      } else if (tid < 2 * LPR) {
+        const float* tv = L.tmv + (tid - LPR) * 8;
+        uint4 wb;
+        wb.x = (__float_as_uint(tv[0]) >> 16) | (__float_as_uint(tv[1]) & 0xffff0000u);
+        wb.y = (__float_as_uint(tv[2]) >> 16) | (__float_as_uint(tv[3]) & 0xffff0000u);
+        wb.z = (__float_as_uint(tv[4]) >> 16) | (__float_as_uint(tv[5]) & 0xffff0000u);
+        wb.w = (__float_as_uint(tv[6]) >> 16) | (__float_as_uint(tv[7]) & 0xffff0000u);
+        *reinterpret_cast<uint4*>(static_cast<KV*>(io.summ.mean_v) + srow * D + (tid - LPR) * 8) = wb;
+      } else if (tid < 2 * LPR + 4) {
+        // group t of 32 channels: each 8-channel slice summed in order, then
+        // the four slices pairwise, as the build sums across its lanes
+        const int t = tid - 2 * LPR;
+        float sl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sl[i] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sl[i] += tvar[(4 * t + i) * 8 + e];
+        }
+        const float gvv = ((sl[0] + sl[1]) + (sl[2] + sl[3])) / ((float)tn * (float)(D / 4));
+        io.summ.gvar[srow * 4 + t] = gvv;
+        L.tgv[t] = gvv;
+      } else if (tid == 2 * LPR + 4 && g == 0) {
+        io.summ.count[(size_t)b * s.max_blocks + M - 1] = tn;
       }
       __syncthreads();
       if (need_mu && wave == ti / 64) {
@@ -622,9 +640,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           }
         }
       }
-      // the stores above are in L2 before the weights go out: the value
-      // workgroup reads the new mean value row only after them
-      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
@@ -652,6 +667,11 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       if (lane == 0) {
         L.mx[j] = mx;
         if (ranked) hdr.put_u64(chunk * G + j, ((uint64_t)__float_as_uint(z) << 32) | __float_as_uint(mx));
+        if constexpr (kApp) {
+          // decode append: wave 0 stored the new summary row; it is in L2
+          // before head 0's chunk max, after which the value workgroup reads it
+          if (app && j == 0) __builtin_amdgcn_s_waitcnt(0);
+        }
         if (comp) wts.put_u64(j * kWStride + kChunk, tagged(mx, tag));
       }
     }
@@ -1141,7 +1161,7 @@ __device__ __forceinline__ void warm_kernel_args() {
 
 template <typename KV, int D, int G, bool kR4, bool kApp>
 __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
-  __shared__ FusedLds<D, G, kApp> lds;
+  __shared__ FusedLds<D, G> lds;
   warm_kernel_args();
   // This workgroup's pair (of the round) and role: control workgroup of
   // chunk `role` (role < n_chunks), else value workgroup role - n_chunks.
