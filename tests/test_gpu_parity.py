@@ -379,53 +379,62 @@ def test_decode_loop_graph_replays_match_eager():
         check_workspace_clean(loop.ws, dims, w.budget_tokens)
 
 
-def _append_step_case(before, num_kv_heads, budget, seed, hot, steps=3):
+def _append_step_case(before, num_kv_heads, budget, seed, hot, steps=3, G=4, d=128, r=4, dtype="bf16"):
     """Inputs for `steps` appending decode steps: sequences of lengths
     `before` get one new token per step.  For sequences listed in `hot` the
     new keys point along the mean query of their KV head, with alternating
     sign and a large norm, so that the tail block (new tokens of very
     different logits) is selected and attended to from the page slots the
     steps just wrote."""
-    G = 4
     w = W.make_decode_inputs(name="append_step", seq_lens=[max(L, 1) for L in before], num_q_heads=G * num_kv_heads,
-                             num_kv_heads=num_kv_heads, head_dim=128, r_groups=4, budget_tokens=budget,
-                             dtype="bf16", n_needles=0, n_outliers=2, extra_capacity_tokens=48, seed=seed)
+                             num_kv_heads=num_kv_heads, head_dim=d, r_groups=r, budget_tokens=budget,
+                             dtype=dtype, n_needles=0, n_outliers=2, extra_capacity_tokens=48, seed=seed)
     dev = to_device(w)
     rng = np.random.default_rng(seed + 100)
     B, H = len(before), num_kv_heads
-    qf = dev.q.float().view(B, H, G, 128).mean(dim=2).cpu().numpy()
-    qf = qf / np.linalg.norm(qf, axis=-1, keepdims=True) * np.sqrt(128)
+    qf = dev.q.float().view(B, H, G, d).mean(dim=2).cpu().numpy()
+    qf = qf / np.linalg.norm(qf, axis=-1, keepdims=True) * np.sqrt(d)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     kv = []
     for t in range(steps):
-        k_new = rng.standard_normal((B, H, 128), dtype=np.float32)
-        v_new = rng.standard_normal((B, H, 128), dtype=np.float32)
+        k_new = rng.standard_normal((B, H, d), dtype=np.float32)
+        v_new = rng.standard_normal((B, H, d), dtype=np.float32)
         for b in hot:
             k_new[b] = (6.0 if t % 2 == 0 else -6.0) * qf[b]
-        kv.append((torch.from_numpy(k_new).to("cuda:0", torch.bfloat16),
-                   torch.from_numpy(v_new).to("cuda:0", torch.bfloat16)))
+        kv.append((torch.from_numpy(k_new).to("cuda:0", tdt), torch.from_numpy(v_new).to("cuda:0", tdt)))
     return w, dev, kv
 
 
-@pytest.mark.parametrize("before,num_kv_heads,budget,hot", [
+@pytest.mark.parametrize("before,num_kv_heads,budget,hot,shape", [
     # tails at slots 8, 0, 15, 1, 0 and 15 of their blocks (the fourth and
     # sixth sequences have every block selected), and one of length 0
-    ([1000, 768, 15, 1, 4096, 31, 0], 2, 64, [0, 1, 4]),
+    ([1000, 768, 15, 1, 4096, 31, 0], 2, 64, [0, 1, 4], {}),
     # one long sequence: 8 chunks per pair, the tail block's reader is
     # another chunk's workgroup
-    ([32767], 8, 512, [0]),
-    ([32768 + 5], 8, 512, []),
+    ([32767], 8, 512, [0], {}),
+    ([32768 + 5], 8, 512, [], {}),
+    # the appending instances for 1, 2 and 8 query heads per KV head
+    ([3000, 767, 16], 2, 128, [0, 1], {"G": 1}),
+    ([3000, 767, 16], 2, 128, [0, 1], {"G": 2}),
+    ([3000, 767, 16], 2, 128, [0, 1], {"G": 8}),
+    # shapes the appending instance does not cover: append, then the step
+    ([3000, 767, 16], 2, 128, [0, 1], {"r": 8}),
+    ([3000, 767, 16], 2, 128, [0, 1], {"d": 64}),
+    ([3000, 767, 16], 2, 128, [0, 1], {"dtype": "f32"}),
 ])
-def test_decode_step_append_matches_append_then_step(before, num_kv_heads, budget, hot):
+def test_decode_step_append_matches_append_then_step(before, num_kv_heads, budget, hot, shape):
     # ckv_decode_step_append against ckv_append_tokens + ckv_decode_step, from
     # the same state: outputs, selections, caches and summaries bit for bit,
     # over three steps in a row (each appending one more token).
-    w, dev, kv = _append_step_case(before, num_kv_heads, budget, seed=41, hot=hot)
+    w, dev, kv = _append_step_case(before, num_kv_heads, budget, seed=41, hot=hot, **shape)
     dims = dev.dims
     summ = C.allocate_summaries(dims, "cuda:0")
     C.build_summaries(dims, dev.k_cache, dev.v_cache, dev.block_table, dev.seq_lens, summ)
-    print(f"[case] decode_step_append lens={before} Hkv={num_kv_heads} budget={budget} "
-          f"launches={C.decode_step_append_launches(dims, budget)}", flush=True)
-    assert C.decode_step_append_launches(dims, budget) == 1
+    launches = C.decode_step_append_launches(dims, budget)
+    print(f"[case] decode_step_append lens={before} Hkv={num_kv_heads} budget={budget} {shape} "
+          f"launches={launches}", flush=True)
+    fusable = shape.get("d", 128) == 128 and shape.get("r", 4) == 4 and shape.get("dtype", "bf16") == "bf16"
+    assert launches == (1 if fusable else 1 + C.decode_step_launches(dims, budget))
 
     def state():
         return (dev.k_cache.clone(), dev.v_cache.clone(),
@@ -436,6 +445,7 @@ def test_decode_step_append_matches_append_then_step(before, num_kv_heads, budge
 
     ka, va, sa = state()
     kb, vb, sb = state()
+    d = dims.head_dim
     wsa = C.allocate_workspace(C.workspace_bytes(dims, budget), "cuda:0")
     wsb = C.allocate_workspace(C.workspace_bytes(dims, budget), "cuda:0")
     for step, (k_new, v_new) in enumerate(kv):
