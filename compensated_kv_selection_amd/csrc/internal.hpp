@@ -13,7 +13,7 @@ constexpr int kChunk = 256;         // blocks scored by one scan workgroup
 constexpr int kSlice = 1024;        // blocks ranked by one select workgroup
 constexpr int kGatherPages = 4;     // selected blocks per gather workgroup (unfused path)
 constexpr int kMaxSplits = 64;      // gather workgroups per (sequence, KV head), unfused path
-constexpr int kDensePages = 32;     // blocks per dense workgroup
+constexpr int kDensePages = 128;    // blocks per dense workgroup
 constexpr int kMaxBlocks = 15872;   // blocks per sequence (page-table width)
 constexpr int kMaxKvHeads = 64;
 constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks + 2 * parts)

@@ -787,6 +787,267 @@ __device__ void merge_role(const Shape& s, const StepIO& io, const Work& w, int 
 }
 
 // ---------------------------------------------------------------------------
+// Dense decode attention (the baseline the sparse step is measured against):
+// exact attention over every block, split over the blocks of each (sequence,
+// KV head) pair, one workgroup per split.  A wave takes whole pages (waves
+// take pages wave, wave + 4, ... of the split).  Each lane holds CPL channels
+// of one token row of the page and keeps its own online-softmax state for
+// the G query heads (maximum in log2 units, sum, CPL accumulators), so the
+// only cross-lane step per token is the LPT-lane sum of each logit.  A
+// lane's maximum is raised only when some lane of the wave meets a larger
+// logit (a wave-uniform branch).  The lanes' states are combined once, at
+// the end of the split; the last split of a pair to arrive merges the
+// splits' partials (the dense mode of merge_role).
+// ---------------------------------------------------------------------------
+template <int D, int G>
+struct DenseCfg {
+  static constexpr int CPL = G == 8 ? 8 : 16;   // channels per lane
+  static constexpr int LPT = D / CPL;           // lanes per token row: 4, 8 or 16
+  static constexpr int TPW = 64 / LPT;          // token rows per wave pass
+  static constexpr int RPP = kBlockSize / TPW;  // rows per lane per page
+  static constexpr int NR = CPL / 8;            // eight-element loads per row
+};
+template <int D, int G>
+struct DenseLds {
+  int pg[kDensePages];
+  int n[kDensePages];
+  union {
+    float red[kThreads / 64][G][D + 4];
+    MergeLds merge;
+  } u;
+};
+
+__device__ __forceinline__ uint32_t dpp_row_half_mirror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_mirror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
+}
+// Sum over each group of LPT consecutive lanes (LPT = 4, 8, 16); every lane
+// of a group receives the same value.
+template <int LPT>
+__device__ __forceinline__ float token_row_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = OpFadd{}(u, dpp_quad_xor1(u));
+  u = OpFadd{}(u, dpp_quad_xor2(u));
+  if (LPT >= 8) u = OpFadd{}(u, dpp_row_half_mirror(u));
+  if (LPT >= 16) u = OpFadd{}(u, dpp_row_mirror(u));
+  return __uint_as_float(u);
+}
+// Reduction over the lanes that hold the same channels (lane % LPT) in the
+// wave's 64 / LPT token slots.
+template <int LPT, class Op>
+__device__ __forceinline__ uint32_t token_slot_reduce(uint32_t x, Op op) {
+  if (LPT == 4) x = op(x, dpp_row_ror4(x));
+  if (LPT <= 8) x = op(x, dpp_row_ror8(x));
+  return across_rows(x, op);
+}
+__device__ __forceinline__ float exp2_from(float a, float m) {  // 2^(a - m), 0 for a = -inf
+  return a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a - m);
+}
+
+template <typename KV, int D, int G>
+__device__ __forceinline__ void dense_issue(const Shape& s, const KV* kc, const KV* vc, int g, int pg, int n,
+                                            int ts, int c, Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                            Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                            bool (&ok)[DenseCfg<D, G>::RPP]) {
+  using C = DenseCfg<D, G>;
+#pragma unroll
+  for (int r = 0; r < C::RPP; ++r) {
+    const int tok = r * C::TPW + ts;
+    ok[r] = pg >= 0 && tok < n;
+    if (ok[r]) {
+      const size_t off = (((size_t)pg * s.Hkv + g) * s.bs + tok) * D + c * C::CPL;
+#pragma unroll
+      for (int u = 0; u < C::NR; ++u) {
+        raw_load(kc + off + 8 * u, kr[r][u]);
+        raw_load(vc + off + 8 * u, vr[r][u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::NR; ++u) {
+        raw_zero(kr[r][u]);
+        raw_zero(vr[r][u]);
+      }
+    }
+  }
+}
+
+template <typename KV, int D, int G>
+__device__ __forceinline__ void dense_page(const float (&qv)[G][DenseCfg<D, G>::CPL], float tl,
+                                           const Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                           const Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                           const bool (&ok)[DenseCfg<D, G>::RPP], float (&m)[G], float (&l)[G],
+                                           float (&acc)[G][DenseCfg<D, G>::CPL]) {
+  using C = DenseCfg<D, G>;
+  constexpr int CPL = C::CPL, RPP = C::RPP;
+  float sc[RPP][G];
+#pragma unroll
+  for (int r = 0; r < RPP; ++r) {
+    float kf[CPL];
+#pragma unroll
+    for (int u = 0; u < C::NR; ++u) raw_float(kr[r][u], *reinterpret_cast<float(*)[8]>(kf + 8 * u));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) d = fmaf(qv[j][e], kf[e], d);
+      d = token_row_sum<C::LPT>(d);
+      sc[r][j] = ok[r] ? d * tl : -INFINITY;
+    }
+  }
+  float p[RPP][G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float mx = sc[0][j];
+#pragma unroll
+    for (int r = 1; r < RPP; ++r) mx = fmaxf(mx, sc[r][j]);
+    if (__ballot(mx > m[j]) != 0) {  // uniform over the wave
+      const float mn = fmaxf(m[j], mx);
+      const float f = exp2_from(m[j], mn);
+      l[j] *= f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[j][e] *= f;
+      m[j] = mn;
+    }
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) {
+      p[r][j] = ok[r] ? __builtin_amdgcn_exp2f(sc[r][j] - m[j]) : 0.f;
+      l[j] += p[r][j];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPP; ++r) {
+    float vf[CPL];
+#pragma unroll
+    for (int u = 0; u < C::NR; ++u) raw_float(vr[r][u], *reinterpret_cast<float(*)[8]>(vf + 8 * u));
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[j][e] = fmaf(p[r][j], vf[e], acc[j][e]);
+  }
+}
+
+template <typename KV, int D, int G>
+__global__ __launch_bounds__(kThreads, 2) void dense_kernel(Shape s, StepIO io, Work w) {
+  using C = DenseCfg<D, G>;
+  constexpr int CPL = C::CPL, LPT = C::LPT, RPP = C::RPP, NR = C::NR, PST = kPartStride(D);
+  constexpr int NW = kThreads / 64;
+  // bf16 pages are double-buffered in registers up to G = 4; otherwise pages
+  // are loaded one at a time
+  constexpr bool kPrefetch = sizeof(KV) == 2 && G <= 4;
+  __shared__ DenseLds<D, G> L;
+  __shared__ uint32_t slot;
+  const int t = (int)blockIdx.x, split = t % s.n_splits, bg = t / s.n_splits;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane % LPT, ts = lane / LPT;
+  const int Lseq = clamp_len(io.seq_lens[b], s.max_blocks * s.bs);
+  const int M = (Lseq + s.bs - 1) / s.bs;
+  const int first = split * s.pages_per_split;
+  const int nb = max(0, min(M, first + s.pages_per_split) - first);
+  for (int e = tid; e < nb; e += kThreads) {
+    const int i = first + e;
+    int p = io.block_table[(size_t)b * s.max_blocks + i];
+    int n = 0;
+    if (p < 0 || p >= s.P) p = -1;
+    else n = min(s.bs, Lseq - i * s.bs);
+    L.pg[e] = p;
+    L.n[e] = n;
+  }
+  const KV* q = static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D + c * CPL;
+  float qv[G][CPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int u = 0; u < NR; ++u) load8(q + (size_t)j * D + 8 * u, *reinterpret_cast<float(*)[8]>(&qv[j][8 * u]));
+  const float tl = s.tau * 1.44269504088896340736f;  // logits in log2 units
+  float m[G], l[G], acc[G][CPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[j][e] = 0.f;
+  }
+  __syncthreads();
+
+  const KV* kc = static_cast<const KV*>(io.k_cache);
+  const KV* vc = static_cast<const KV*>(io.v_cache);
+  const int np = nb > wave ? (nb - 1 - wave) / NW + 1 : 0;  // this wave's pages: wave + NW i
+  Raw8<KV> ka[RPP][NR], va[RPP][NR];
+  bool oka[RPP];
+  if constexpr (kPrefetch) {
+    Raw8<KV> kb[RPP][NR], vb[RPP][NR];
+    bool okb[RPP];
+    if (np > 0) dense_issue<KV, D, G>(s, kc, vc, g, L.pg[wave], L.n[wave], ts, c, ka, va, oka);
+    for (int pi = 0; pi < np; pi += 2) {
+      if (pi + 1 < np) {
+        const int bl = wave + NW * (pi + 1);
+        dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, kb, vb, okb);
+      }
+      dense_page<KV, D, G>(qv, tl, ka, va, oka, m, l, acc);
+      if (pi + 1 < np) {
+        if (pi + 2 < np) {
+          const int bl = wave + NW * (pi + 2);
+          dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, ka, va, oka);
+        }
+        dense_page<KV, D, G>(qv, tl, kb, vb, okb, m, l, acc);
+      }
+    }
+  } else {
+    for (int pi = 0; pi < np; ++pi) {
+      const int bl = wave + NW * pi;
+      dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, ka, va, oka);
+      dense_page<KV, D, G>(qv, tl, ka, va, oka, m, l, acc);
+    }
+  }
+
+  // combine the token slots of the wave, then the waves, into one partial
+  // per head: [max (natural log units), sum, -, -, acc[D]]
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float mw = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(m[j]), OpFmax{}));
+    const float f = exp2_from(m[j], mw);
+    const float lw = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(l[j] * f), OpFadd{}));
+    float a[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) a[e] = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(acc[j][e] * f), OpFadd{}));
+    if (lane < LPT) {
+      float* rw = L.u.red[wave][j];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) rw[4 + c * CPL + e] = a[e];
+      if (c == 0) {
+        rw[0] = mw;
+        rw[1] = lw;
+      }
+    }
+  }
+  __syncthreads();
+  const Coh part(w.gpart + ((size_t)bg * s.n_splits + split) * G * PST, (size_t)G * PST * 4);
+  for (int o = tid; o < G * D; o += kThreads) {
+    const int j = o / D, d = o % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, L.u.red[v][j][0]);
+    float a = 0.f, ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float f = exp2_from(L.u.red[v][j][0], Mx);
+      a = fmaf(L.u.red[v][j][4 + d], f, a);
+      ls = fmaf(L.u.red[v][j][1], f, ls);
+    }
+    part.put(j * PST + 4 + d, a);
+    if (d == 0) {
+      part.put(j * PST, Mx * 0.69314718055994530942f);  // -inf stays -inf
+      part.put(j * PST + 1, ls);
+    }
+  }
+  const uint32_t prev = arrive(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 2, &slot);
+  if (prev == (uint32_t)(s.n_splits - 1)) merge_role<D, G, kModeDense>(s, io, w, bg, L.u.merge);
+}
+
+// ---------------------------------------------------------------------------
 // The step kernel.  blockIdx.x: [scans], [slices] or [gathers], by mode.
 // ---------------------------------------------------------------------------
 template <typename KV, int D, int G, int MODE>
@@ -877,12 +1138,30 @@ static hipError_t launch_mode(const Shape& s, const StepIO& io, const Work& w, h
   });
 }
 
+static hipError_t launch_dense(const Shape& s, const StepIO& io, const Work& w, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * s.n_splits);
+#define CKV_DG(KV, DD)                                                                                  \
+  switch (s.G) {                                                                                        \
+    case 1: hipLaunchKernelGGL((dense_kernel<KV, DD, 1>), grid, dim3(kThreads), 0, st, s, io, w); break; \
+    case 2: hipLaunchKernelGGL((dense_kernel<KV, DD, 2>), grid, dim3(kThreads), 0, st, s, io, w); break; \
+    case 4: hipLaunchKernelGGL((dense_kernel<KV, DD, 4>), grid, dim3(kThreads), 0, st, s, io, w); break; \
+    default: hipLaunchKernelGGL((dense_kernel<KV, DD, 8>), grid, dim3(kThreads), 0, st, s, io, w); break; \
+  }
+  if (s.dtype == 0) {
+    if (s.D == 128) { CKV_DG(uint16_t, 128) } else { CKV_DG(uint16_t, 64) }
+  } else {
+    if (s.D == 128) { CKV_DG(float, 128) } else { CKV_DG(float, 64) }
+  }
+#undef CKV_DG
+  return hipGetLastError();
+}
+
 hipError_t launch_step(const Shape& s, int mode, const StepIO& io, const Work& w, hipStream_t st) {
   switch (mode) {
     case kModeScanOnly: return launch_mode<kModeScanOnly>(s, io, w, st);
     case kModeSelectOnly: return launch_mode<kModeSelectOnly>(s, io, w, st);
     case kModeAttendOnly: return launch_mode<kModeAttendOnly>(s, io, w, st);
-    case kModeDense: return launch_mode<kModeDense>(s, io, w, st);
+    case kModeDense: return launch_dense(s, io, w, st);
     default: return hipErrorInvalidValue;
   }
 }

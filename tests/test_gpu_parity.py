@@ -132,6 +132,41 @@ def test_constant_key_blocks_give_dense_output():
         assert np.abs(g.lse[b] - lse).max() <= 1e-4
 
 
+def _dense_check(w):
+    print(f"[case] dense {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+          f"d={w.head_dim} {w.dtype} lens={list(w.seq_lens)[:6]}", flush=True)
+    dev = to_device(w)
+    ws = C.allocate_workspace(C.dense_workspace_bytes(dev.dims), "cuda:0")
+    worst = 0.0
+    for rep in range(2):  # the second call reuses the workspace (arrival counters reset)
+        out, lse = C.dense_decode_attention(dev.dims, dev.q, dev.k_cache, dev.v_cache, dev.block_table,
+                                            dev.seq_lens, ws)
+        torch.cuda.synchronize()
+        out, lse = out.cpu().numpy(), lse.cpu().numpy()
+        for b in range(w.batch):
+            q, k, v = O.sequence_arrays(w.q[b], w.k_tokens[b], w.v_tokens[b], w.dtype)
+            ro, rl = O.dense_attention(q, k, v)
+            err = float(np.abs(out[b] - ro).max())
+            worst = max(worst, err)
+            assert err <= 2e-3, (b, err)
+            assert np.abs(lse[b] - rl).max() <= 1e-4
+    print(f"[case] ok: dense max |out - oracle| = {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (2, 64, "f32"), (4, 64, "bf16"), (8, 128, "bf16"),
+                                       (8, 64, "f32"), (4, 128, "f32"), (2, 128, "bf16"), (8, 128, "f32")])
+def test_dense_head_layouts(G, d, dtype):
+    # lengths cover a split boundary (128 blocks = 2048 tokens), ragged tails
+    # and a one-token sequence
+    w = small_gqa(seed=10 + G, seq_lens=[2049, 2047, 17, 1, 5000], num_q_heads=2 * G, head_dim=d,
+                  dtype=dtype)
+    _dense_check(w)
+
+
+def test_dense_llama_32k():
+    _dense_check(W.make_preset("llama_32k", seed=1))
+
+
 def test_dense_kernel_matches_oracle():
     w = small_gqa(seed=9)
     dev = to_device(w)
