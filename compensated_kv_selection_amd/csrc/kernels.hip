@@ -873,8 +873,19 @@ __device__ __forceinline__ void dense_issue(const Shape& s, const KV* kc, const 
   }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ uint32_t raw_word(const Raw8<uint16_t>& r, int i) {
+  return i == 0 ? r.a.x : i == 1 ? r.a.y : i == 2 ? r.a.z : r.a.w;
+}
+
+// qv: the G query rows' CPL channels as float (f32 caches); qp: the same as
+// bf16 pairs (bf16 caches, whose logits use the two-term bf16 dot product).
 template <typename KV, int D, int G>
-__device__ __forceinline__ void dense_page(const float (&qv)[G][DenseCfg<D, G>::CPL], float tl,
+__device__ __forceinline__ void dense_page(const float (&qv)[G][DenseCfg<D, G>::CPL],
+                                           const uint32_t (&qp)[G][DenseCfg<D, G>::CPL / 2], float tl,
                                            const Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
                                            const Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
                                            const bool (&ok)[DenseCfg<D, G>::RPP], float (&m)[G], float (&l)[G],
@@ -884,15 +895,32 @@ __device__ __forceinline__ void dense_page(const float (&qv)[G][DenseCfg<D, G>::
   float sc[RPP][G];
 #pragma unroll
   for (int r = 0; r < RPP; ++r) {
-    float kf[CPL];
+    float dd[G];
+    if constexpr (sizeof(KV) == 2) {
 #pragma unroll
-    for (int u = 0; u < C::NR; ++u) raw_float(kr[r][u], *reinterpret_cast<float(*)[8]>(kf + 8 * u));
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int u = 0; u < C::NR; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d = dot2_bf16(raw_word(kr[r][u], i), qp[j][4 * u + i], d);
+        dd[j] = d;
+      }
+    } else {
+      float kf[CPL];
+#pragma unroll
+      for (int u = 0; u < C::NR; ++u) raw_float(kr[r][u], *reinterpret_cast<float(*)[8]>(kf + 8 * u));
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) d = fmaf(qv[j][e], kf[e], d);
+        dd[j] = d;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) d = fmaf(qv[j][e], kf[e], d);
-      d = token_row_sum<C::LPT>(d);
+      const float d = token_row_sum<C::LPT>(dd[j]);
       sc[r][j] = ok[r] ? d * tl : -INFINITY;
     }
   }
@@ -957,10 +985,20 @@ __global__ __launch_bounds__(kThreads, 2) void dense_kernel(Shape s, StepIO io, 
   }
   const KV* q = static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D + c * CPL;
   float qv[G][CPL];
+  uint32_t qp[G][CPL / 2];
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int u = 0; u < NR; ++u) load8(q + (size_t)j * D + 8 * u, *reinterpret_cast<float(*)[8]>(&qv[j][8 * u]));
+    for (int u = 0; u < NR; ++u) {
+      if constexpr (sizeof(KV) == 2) {
+        Raw8<KV> rq;
+        raw_load(q + (size_t)j * D + 8 * u, rq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qp[j][4 * u + i] = raw_word(rq, i);
+      } else {
+        load8(q + (size_t)j * D + 8 * u, *reinterpret_cast<float(*)[8]>(&qv[j][8 * u]));
+      }
+    }
   const float tl = s.tau * 1.44269504088896340736f;  // logits in log2 units
   float m[G], l[G], acc[G][CPL];
 #pragma unroll
@@ -986,20 +1024,20 @@ __global__ __launch_bounds__(kThreads, 2) void dense_kernel(Shape s, StepIO io, 
         const int bl = wave + NW * (pi + 1);
         dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, kb, vb, okb);
       }
-      dense_page<KV, D, G>(qv, tl, ka, va, oka, m, l, acc);
+      dense_page<KV, D, G>(qv, qp, tl, ka, va, oka, m, l, acc);
       if (pi + 1 < np) {
         if (pi + 2 < np) {
           const int bl = wave + NW * (pi + 2);
           dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, ka, va, oka);
         }
-        dense_page<KV, D, G>(qv, tl, kb, vb, okb, m, l, acc);
+        dense_page<KV, D, G>(qv, qp, tl, kb, vb, okb, m, l, acc);
       }
     }
   } else {
     for (int pi = 0; pi < np; ++pi) {
       const int bl = wave + NW * pi;
       dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, ka, va, oka);
-      dense_page<KV, D, G>(qv, tl, ka, va, oka, m, l, acc);
+      dense_page<KV, D, G>(qv, qp, tl, ka, va, oka, m, l, acc);
     }
   }
 
