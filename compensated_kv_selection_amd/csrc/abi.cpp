@@ -141,9 +141,19 @@ ckv::Work carve(const ckv::Shape& s, void* ws) {
                    reinterpret_cast<uint64_t*>(base + L.fpart)};
 }
 
+// Dense splits: about 256 workgroups in all (one per CU), a
+// multiple of 4 blocks (one per wave) between 8 and kDensePages blocks each,
+// and at most 256 splits per (sequence, KV head) so that the merge's factors
+// fit its LDS.  Depends on the dims only, so the workspace size does too.
 void set_dense(ckv::Shape& s) {
-  s.pages_per_split = ckv::kDensePages;
-  s.n_splits = (s.max_blocks + ckv::kDensePages - 1) / ckv::kDensePages;
+  const long long pairs = (long long)s.B * s.Hkv;
+  long long pps = (pairs * s.max_blocks + 255) / 256;
+  pps = (pps + 3) / 4 * 4;
+  const long long floor_pps = std::max<long long>(8, (s.max_blocks + 255) / 256);
+  pps = std::max(pps, (floor_pps + 3) / 4 * 4);
+  pps = std::min<long long>(pps, ckv::kDensePages);
+  s.pages_per_split = (int)pps;
+  s.n_splits = (s.max_blocks + s.pages_per_split - 1) / s.pages_per_split;
 }
 
 size_t dense_bytes(const ckv::Shape& s) {

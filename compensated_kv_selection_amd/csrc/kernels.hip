@@ -50,6 +50,18 @@ constexpr int kThreads = 256;
 // rows (kn, vn: [B][Hkv][D]) are written into the page and used in place of
 // what the page held there.
 // ---------------------------------------------------------------------------
+// Streaming loads of the caches (each page is read once per build).
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load16(const void* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void raw_load_nt(const uint16_t* p, Raw8<uint16_t>& r) { r.a = nt_load16(p); }
+__device__ __forceinline__ void raw_load_nt(const float* p, Raw8<float>& r) {
+  r.a = nt_load16(p);
+  r.b = nt_load16(p + 4);
+}
+
 template <typename KV, int D>
 __global__ __launch_bounds__(kThreads) void summary_kernel(
     Shape s, KV* kc, KV* vc, const int32_t* __restrict__ bt, const int32_t* __restrict__ sl,
@@ -83,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(
     KV* p = (isv ? vc : kc) + ((size_t)page * s.Hkv + g) * s.bs * D + c * 8;
     Raw8<KV> raw[kBlockSize];
 #pragma unroll
-    for (int t = 0; t < kBlockSize; ++t) raw_load(p + t * D, raw[t]);
+    for (int t = 0; t < kBlockSize; ++t) raw_load_nt(p + t * D, raw[t]);
     if (kn) {  // the new token is row n - 1; only this thread touches its 8 channels
       Raw8<KV> nr;
       raw_load((isv ? vn : kn) + ((size_t)b * s.Hkv + g) * D + c * 8, nr);

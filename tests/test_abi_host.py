@@ -172,7 +172,22 @@ def test_workspace_size_formula(lib):
         expect = sum(workspace_regions(1, 32, 8, 128, 8192, budget))
         assert ws_bytes(lib, d, budget) == expect, budget
     ctrl = workspace_regions(1, 32, 8, 128, 8192, 0)[0]
-    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + (8 * 256 * 4 * 132 * 4 + 255) // 256 * 256
+    # dense: 8192 blocks per pair in splits of 128 blocks (the cap) -> 64 splits
+    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + (8 * 64 * 4 * 132 * 4 + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("batch,kv_heads,max_blocks,splits", [
+    (1, 8, 8192, 64),    # 128-block splits (the cap)
+    (1, 8, 2048, 32),    # 64-block splits: about 256 workgroups
+    (1, 1, 256, 32),     # 8-block splits (the floor)
+    (1, 1, 15872, 248),  # at most 256 splits per pair: 64-block splits
+    (16, 8, 4096, 32),   # a large batch: 128-block splits
+])
+def test_dense_split_rule(lib, batch, kv_heads, max_blocks, splits):
+    d = good_dims(batch=batch, num_q_heads=4 * kv_heads, num_kv_heads=kv_heads, max_blocks_per_seq=max_blocks)
+    ctrl = workspace_regions(batch, 4 * kv_heads, kv_heads, 128, max_blocks, 0)[0]
+    part = batch * kv_heads * splits * 4 * 132 * 4
+    assert lib.ckv_dense_workspace_bytes(ctypes.byref(d)) == ctrl + (part + 255) // 256 * 256
 
 
 def test_errors_leave_no_stale_message_after_success_path_text(lib):

@@ -167,6 +167,11 @@ def test_dense_llama_32k():
     _dense_check(W.make_preset("llama_32k", seed=1))
 
 
+def test_dense_llama_128k():
+    # the benchmarked launch: 128-block splits, one round of 512 workgroups
+    _dense_check(W.make_preset("llama_128k", seed=2))
+
+
 def test_dense_kernel_matches_oracle():
     w = small_gqa(seed=9)
     dev = to_device(w)
