@@ -77,6 +77,7 @@ def ws_bytes(lib, dims, budget=512):
     (dict(num_pages=0), INVALID, "num_pages"),
     (dict(max_blocks_per_seq=0), INVALID, "max_blocks"),
     (dict(max_blocks_per_seq=20000), UNSUPPORTED, "max_blocks"),
+    (dict(max_blocks_per_seq=15873, num_pages=15873), UNSUPPORTED, "max_blocks"),  # one past the widest table
     (dict(kv_dtype=7), INVALID, "kv_dtype"),
 ])
 def test_bad_dims_rejected_everywhere(lib, kw, status, needle):

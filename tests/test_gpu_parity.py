@@ -258,6 +258,17 @@ def test_llama_32k():
     full_check(W.make_preset("llama_32k", seed=0), fused=True)
 
 
+def test_max_context_length():
+    # The widest page table the library takes (15872 blocks, 253952 tokens),
+    # one token short so the last block is ragged: the single-launch step, the
+    # three-launch path and dense decode, against the oracle.
+    w = W.make_decode_inputs(name="max_ctx", seq_lens=[253951], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                             r_groups=4, budget_tokens=512, dtype="bf16", n_needles=8, n_outliers=4, seed=21)
+    assert w.max_blocks == 15872
+    full_check(w)
+    _dense_check(w)
+
+
 @pytest.mark.parametrize("across_xcds", [False, True])
 def test_fused_step_both_placements(across_xcds, monkeypatch):
     # By default a pair's workgroups share one XCD and hand data over through
