@@ -442,7 +442,18 @@ def main() -> int:
     launches = C.decode_step_launches(dims, budget)
     per_launch_us = np.array([us_per_step])
 
-    ab = algorithmic_bytes(M, w.num_kv_heads, w.head_dim, w.r_groups, kk, w.block_size, kv_bytes)
+    # summed over the batch's sequences (each with its own block count)
+    ab = {"summary": 0, "selected_kv": 0, "total": 0}
+    for Lb in w.seq_lens:
+        Mb = -(-int(Lb) // w.block_size)
+        abb = algorithmic_bytes(Mb, w.num_kv_heads, w.head_dim, w.r_groups, min(Mb, budget // w.block_size),
+                                w.block_size, kv_bytes)
+        for key in ab:
+            ab[key] += abb[key]
+    kv_all = sum(-(-int(Lb) // w.block_size) for Lb in w.seq_lens) * w.num_kv_heads * w.block_size * w.head_dim \
+        * 2 * kv_bytes  # every page's keys and values
+    tokens_desc = (f"{L} tokens" if w.batch == 1 else
+                   f"{int(w.seq_lens.min())} to {L} tokens per sequence ({int(w.seq_lens.sum())} in all)")
     avg_launch_us = float(per_launch_us.mean())
     achieved = ab["total"] / (avg_launch_us * 1e-6) / 1e9
     eff_gbps = ab["total"] / (us_per_step * 1e-6) / 1e9
@@ -471,7 +482,7 @@ def main() -> int:
         e1.record()
         torch.cuda.synchronize()
         dense_us = e0.elapsed_time(e1) * 1e3 / dn
-        dense_bytes = M * w.num_kv_heads * w.block_size * w.head_dim * 2 * kv_bytes
+        dense_bytes = kv_all
         dense = {"us_per_step": round(dense_us, 2), "bytes": dense_bytes,
                  "GBps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
                  "speedup_of_compkv": round(dense_us / us_per_step, 2)}
@@ -505,7 +516,7 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_per_step / 1e3, 6),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: decode step, batch {w.batch}, {L} tokens, Hq "
+        "config": {"workload": f"{args.workload}: decode step, batch {w.batch}, {tokens_desc}, Hq "
                                f"{w.num_q_heads}, Hkv {w.num_kv_heads}, d {w.head_dim}, block "
                                f"{w.block_size}, r {w.r_groups}, budget {budget} tokens ({kk} blocks), "
                                f"{args.layers} rotating layer buffers",
@@ -513,10 +524,8 @@ def main() -> int:
         "effective_GBps": round(eff_gbps, 1), "pct_hbm_peak": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes": ab, "roofline": roof, "dense": dense,
         "summary_build": {"us": round(build_us, 1),
-                          "bytes": M * w.num_kv_heads * w.block_size * w.head_dim * 2 * kv_bytes
-                          + ab["summary"],
-                          "GBps": round((M * w.num_kv_heads * w.block_size * w.head_dim * 2 * kv_bytes
-                                         + ab["summary"]) / (build_us * 1e-6) / 1e9, 1)},
+                          "bytes": kv_all + ab["summary"],
+                          "GBps": round((kv_all + ab["summary"]) / (build_us * 1e-6) / 1e9, 1)},
         "cpu_baseline": cpu, "kernel_source_hash": src_hash,
     }
     print(json.dumps(line), flush=True)
