@@ -194,14 +194,14 @@ ckv::Summ to_summ(const ckv_summaries* sm) {
 
 // Value workgroups per pair and pairs per round when `pairs` pairs share
 // `cap` resident workgroups: the fewest rounds, then the most value
-// workgroups (one per chunk, down to one per two chunks).  rounds == 0: not
+// workgroups (one per chunk, down to one per four chunks).  rounds == 0: not
 // even one pair fits.
 struct Fit {
   int n_val = 0, per_round = 0, rounds = 0;
 };
 Fit fit_pairs(int n_chunks, int cap, int pairs) {
   Fit best;
-  for (int nv = n_chunks; nv >= (n_chunks + 1) / 2; --nv) {
+  for (int nv = n_chunks; nv >= (n_chunks + 3) / 4; --nv) {
     const int per = std::min(pairs, cap / (n_chunks + nv));
     if (per < 1) continue;
     const int rounds = (pairs + per - 1) / per;
@@ -211,7 +211,7 @@ Fit fit_pairs(int n_chunks, int cap, int pairs) {
 }
 
 // One launch when its whole grid - at least the control workgroups of every
-// chunk of one (sequence, KV head) pair and a value workgroup per two chunks -
+// chunk of one (sequence, KV head) pair and a value workgroup per four chunks -
 // can be resident at once, the pair's candidates fit in shared memory and page
 // ids fit in its selection keys; otherwise three launches that never wait.
 // Sets s->bg_round (pairs per round of the persistent grid) and s->n_val when

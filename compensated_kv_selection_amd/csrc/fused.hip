@@ -15,7 +15,7 @@
 // Organisation.  Every (sequence, KV head) pair is split into chunks of 256
 // blocks.  Every chunk gets a control workgroup of 4 waves, and the pair gets
 // n_val value workgroups of 4 waves: one per chunk when the whole grid fits on
-// the device at once, else as few as make it fit (down to one per two
+// the device at once, else as few as make it fit (down to one per four
 // chunks), value workgroup v taking chunks v, v + n_val, ... in turn:
 //   a control workgroup loads the chunk's mean keys, grouped variances and
 //     page-table entries, computes the block-mean logits on the matrix cores
