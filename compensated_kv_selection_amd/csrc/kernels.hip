@@ -174,6 +174,7 @@ struct GathLds {
   int n[kShareMax];
   float st[2 * RS * G];
   float acc[RS * D];
+  float red[kThreads / 64][G][D + 4];  // the exact tokens' per-wave states
 };
 struct MergeLds {
   float f[kMergeFactors];
@@ -576,18 +577,283 @@ __device__ void combine_online(const float (&m)[G], const float (&l)[G], const f
   }
 }
 
+template <int D, int G>
+struct DenseCfg {
+  static constexpr int CPL = G == 8 ? 8 : 16;   // channels per lane
+  static constexpr int LPT = D / CPL;           // lanes per token row: 4, 8 or 16
+  static constexpr int TPW = 64 / LPT;          // token rows per wave pass
+  static constexpr int RPP = kBlockSize / TPW;  // rows per lane per page
+  static constexpr int NR = CPL / 8;            // eight-element loads per row
+};
+
+__device__ __forceinline__ uint32_t dpp_row_half_mirror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_mirror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
+}
+// Sum over each group of LPT consecutive lanes (LPT = 4, 8, 16); every lane
+// of a group receives the same value.
+template <int LPT>
+__device__ __forceinline__ float token_row_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = OpFadd{}(u, dpp_quad_xor1(u));
+  u = OpFadd{}(u, dpp_quad_xor2(u));
+  if (LPT >= 8) u = OpFadd{}(u, dpp_row_half_mirror(u));
+  if (LPT >= 16) u = OpFadd{}(u, dpp_row_mirror(u));
+  return __uint_as_float(u);
+}
+// Reduction over the lanes that hold the same channels (lane % LPT) in the
+// wave's 64 / LPT token slots.
+template <int LPT, class Op>
+__device__ __forceinline__ uint32_t token_slot_reduce(uint32_t x, Op op) {
+  if (LPT == 4) x = op(x, dpp_row_ror4(x));
+  if (LPT <= 8) x = op(x, dpp_row_ror8(x));
+  return across_rows(x, op);
+}
+__device__ __forceinline__ float exp2_from(float a, float m) {  // 2^(a - m), 0 for a = -inf
+  return a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a - m);
+}
+
+template <typename KV, int D, int G>
+__device__ __forceinline__ void dense_issue(const Shape& s, const KV* kc, const KV* vc, int g, int pg, int n,
+                                            int ts, int c, Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                            Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                            bool (&ok)[DenseCfg<D, G>::RPP]) {
+  using C = DenseCfg<D, G>;
+#pragma unroll
+  for (int r = 0; r < C::RPP; ++r) {
+    const int tok = r * C::TPW + ts;
+    ok[r] = pg >= 0 && tok < n;
+    if (ok[r]) {
+      const size_t off = (((size_t)pg * s.Hkv + g) * s.bs + tok) * D + c * C::CPL;
+#pragma unroll
+      for (int u = 0; u < C::NR; ++u) {
+        raw_load(kc + off + 8 * u, kr[r][u]);
+        raw_load(vc + off + 8 * u, vr[r][u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::NR; ++u) {
+        raw_zero(kr[r][u]);
+        raw_zero(vr[r][u]);
+      }
+    }
+  }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ uint32_t raw_word(const Raw8<uint16_t>& r, int i) {
+  return i == 0 ? r.a.x : i == 1 ? r.a.y : i == 2 ? r.a.z : r.a.w;
+}
+
+// qv: the G query rows' CPL channels as float (f32 caches); qp: the same as
+// bf16 pairs (bf16 caches, whose logits use the two-term bf16 dot product).
+template <typename KV, int D, int G>
+__device__ __forceinline__ void dense_page(const float (&qv)[G][DenseCfg<D, G>::CPL],
+                                           const uint32_t (&qp)[G][DenseCfg<D, G>::CPL / 2], float tl,
+                                           const Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                           const Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
+                                           const bool (&ok)[DenseCfg<D, G>::RPP], float (&m)[G], float (&l)[G],
+                                           float (&acc)[G][DenseCfg<D, G>::CPL]) {
+  using C = DenseCfg<D, G>;
+  constexpr int CPL = C::CPL, RPP = C::RPP;
+  float sc[RPP][G];
+#pragma unroll
+  for (int r = 0; r < RPP; ++r) {
+    float dd[G];
+    if constexpr (sizeof(KV) == 2) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int u = 0; u < C::NR; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d = dot2_bf16(raw_word(kr[r][u], i), qp[j][4 * u + i], d);
+        dd[j] = d;
+      }
+    } else {
+      float kf[CPL];
+#pragma unroll
+      for (int u = 0; u < C::NR; ++u) raw_float(kr[r][u], *reinterpret_cast<float(*)[8]>(kf + 8 * u));
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) d = fmaf(qv[j][e], kf[e], d);
+        dd[j] = d;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float d = token_row_sum<C::LPT>(dd[j]);
+      sc[r][j] = ok[r] ? d * tl : -INFINITY;
+    }
+  }
+  float p[RPP][G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float mx = sc[0][j];
+#pragma unroll
+    for (int r = 1; r < RPP; ++r) mx = fmaxf(mx, sc[r][j]);
+    if (__ballot(mx > m[j]) != 0) {  // uniform over the wave
+      const float mn = fmaxf(m[j], mx);
+      const float f = exp2_from(m[j], mn);
+      l[j] *= f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[j][e] *= f;
+      m[j] = mn;
+    }
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) {
+      p[r][j] = ok[r] ? __builtin_amdgcn_exp2f(sc[r][j] - m[j]) : 0.f;
+      l[j] += p[r][j];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPP; ++r) {
+    float vf[CPL];
+#pragma unroll
+    for (int u = 0; u < C::NR; ++u) raw_float(vr[r][u], *reinterpret_cast<float(*)[8]>(vf + 8 * u));
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) acc[j][e] = fmaf(p[r][j], vf[e], acc[j][e]);
+  }
+}
+
+// Exact attention of the G query heads of KV head g of sequence b over nb
+// pages (page ids pg[], -1 = none, and token counts n[], in LDS, written
+// before a barrier) into one partial per head at part: [max (natural log
+// units), sum, -, -, acc[D]], head stride head_stride floats, device-coherent
+// stores.  The waves take pages wave, wave + 4, ...; each lane holds CPL
+// channels of one token row and keeps its own online softmax for the G heads
+// (maximum in log2 units), raised only when some lane of the wave meets a
+// larger logit; the lanes' states are combined once, at the end, through
+// red (LDS).
+template <typename KV, int D, int G>
+__device__ __forceinline__ void dense_span(const Shape& s, const StepIO& io, int b, int g, const int* pg,
+                                           const int* n, int nb, float (*red)[G][D + 4], float* part,
+                                           int head_stride) {
+  using C = DenseCfg<D, G>;
+  constexpr int CPL = C::CPL, LPT = C::LPT, RPP = C::RPP, NR = C::NR, PST = kPartStride(D);
+  constexpr int NW = kThreads / 64;
+  // bf16 pages are double-buffered in registers up to G = 4; otherwise pages
+  // are loaded one at a time
+  constexpr bool kPrefetch = sizeof(KV) == 2 && G <= 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane % LPT, ts = lane / LPT;
+  const KV* q = static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D + c * CPL;
+  float qv[G][CPL];
+  uint32_t qp[G][CPL / 2];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      if constexpr (sizeof(KV) == 2) {
+        Raw8<KV> rq;
+        raw_load(q + (size_t)j * D + 8 * u, rq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qp[j][4 * u + i] = raw_word(rq, i);
+      } else {
+        load8(q + (size_t)j * D + 8 * u, *reinterpret_cast<float(*)[8]>(&qv[j][8 * u]));
+      }
+    }
+  const float tl = s.tau * 1.44269504088896340736f;  // logits in log2 units
+  float m[G], l[G], acc[G][CPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[j][e] = 0.f;
+  }
+
+  const KV* kc = static_cast<const KV*>(io.k_cache);
+  const KV* vc = static_cast<const KV*>(io.v_cache);
+  const int np = nb > wave ? (nb - 1 - wave) / NW + 1 : 0;  // this wave's pages: wave + NW i
+  Raw8<KV> ka[RPP][NR], va[RPP][NR];
+  bool oka[RPP];
+  if constexpr (kPrefetch) {
+    Raw8<KV> kb[RPP][NR], vb[RPP][NR];
+    bool okb[RPP];
+    if (np > 0) dense_issue<KV, D, G>(s, kc, vc, g, pg[wave], n[wave], ts, c, ka, va, oka);
+    for (int pi = 0; pi < np; pi += 2) {
+      if (pi + 1 < np) {
+        const int bl = wave + NW * (pi + 1);
+        dense_issue<KV, D, G>(s, kc, vc, g, pg[bl], n[bl], ts, c, kb, vb, okb);
+      }
+      dense_page<KV, D, G>(qv, qp, tl, ka, va, oka, m, l, acc);
+      if (pi + 1 < np) {
+        if (pi + 2 < np) {
+          const int bl = wave + NW * (pi + 2);
+          dense_issue<KV, D, G>(s, kc, vc, g, pg[bl], n[bl], ts, c, ka, va, oka);
+        }
+        dense_page<KV, D, G>(qv, qp, tl, kb, vb, okb, m, l, acc);
+      }
+    }
+  } else {
+    for (int pi = 0; pi < np; ++pi) {
+      const int bl = wave + NW * pi;
+      dense_issue<KV, D, G>(s, kc, vc, g, pg[bl], n[bl], ts, c, ka, va, oka);
+      dense_page<KV, D, G>(qv, qp, tl, ka, va, oka, m, l, acc);
+    }
+  }
+
+  // combine the token slots of the wave, then the waves, into one partial
+  // per head: [max (natural log units), sum, -, -, acc[D]]
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float mw = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(m[j]), OpFmax{}));
+    const float f = exp2_from(m[j], mw);
+    const float lw = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(l[j] * f), OpFadd{}));
+    float a[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) a[e] = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(acc[j][e] * f), OpFadd{}));
+    if (lane < LPT) {
+      float* rw = red[wave][j];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) rw[4 + c * CPL + e] = a[e];
+      if (c == 0) {
+        rw[0] = mw;
+        rw[1] = lw;
+      }
+    }
+  }
+  __syncthreads();
+  const Coh out(part, (size_t)(G - 1) * head_stride * 4 + (size_t)PST * 4);
+  for (int o = tid; o < G * D; o += kThreads) {
+    const int j = o / D, d = o % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, red[v][j][0]);
+    float a = 0.f, ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float f = exp2_from(red[v][j][0], Mx);
+      a = fmaf(red[v][j][4 + d], f, a);
+      ls = fmaf(red[v][j][1], f, ls);
+    }
+    out.put(j * head_stride + 4 + d, a);
+    if (d == 0) {
+      out.put(j * head_stride, Mx * 0.69314718055994530942f);  // -inf stays -inf
+      out.put(j * head_stride + 1, ls);
+    }
+  }
+}
+
 template <typename KV, int D, int G>
 __device__ void gather_core(const Shape& s, const StepIO& io, int b, int g, const int* blk, int nb,
                             bool comp, float* part, int slot, GathLds<D, G>& L) {
   constexpr int LPR = D / 8, RS = kThreads / LPR, PST = kPartStride(D);
-  constexpr int UG = 4;  // rows per lane per batch
   const int bg = b * s.Hkv + g;
   const int tid = threadIdx.x, rs = tid / LPR, c = tid % LPR;
   const int Lseq = clamp_len(io.seq_lens[b], s.max_blocks * s.bs);
   const int M = (Lseq + s.bs - 1) / s.bs;
   const KV* q = static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D;
-  const KV* kc = static_cast<const KV*>(io.k_cache);
-  const KV* vc = static_cast<const KV*>(io.v_cache);
 
   for (int e = tid; e < nb; e += kThreads) {
     const int i = blk[e];
@@ -605,55 +871,9 @@ __device__ void gather_core(const Shape& s, const StepIO& io, int b, int g, cons
   for (int j = 0; j < G; ++j) load8(q + (size_t)j * D + c * 8, qv[j]);
   __syncthreads();
 
+  // exact tokens of the listed pages
+  dense_span<KV, D, G>(s, io, b, g, L.pg, L.n, nb, L.red, part, slot);
   float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-  }
-  const int nrows = nb * kBlockSize;
-  const int nbatch = (nrows + RS * UG - 1) / (RS * UG);
-  Raw8<KV> kr[UG], vr[UG];
-  bool ok[UG];
-  // software pipeline: the next batch is in flight while this one is used
-#define CKV_ISSUE(BI)                                                                     \
-  _Pragma("unroll") for (int u = 0; u < UG; ++u) {                                        \
-    const int R = ((BI) * UG + u) * RS + rs;                                              \
-    const int bl = R / kBlockSize, tok = R % kBlockSize;                                  \
-    ok[u] = R < nrows && L.pg[bl] >= 0 && tok < L.n[bl];                                  \
-    if (ok[u]) {                                                                          \
-      const size_t off = (((size_t)L.pg[bl] * s.Hkv + g) * s.bs + tok) * D + c * 8;       \
-      raw_load(kc + off, kr[u]);                                                          \
-      raw_load(vc + off, vr[u]);                                                          \
-    }                                                                                     \
-  }
-  if (nbatch > 0) { CKV_ISSUE(0) }
-  for (int bi = 0; bi < nbatch; ++bi) {
-    float k8[UG][8], v8[UG][8];
-    bool okc[UG];
-#pragma unroll
-    for (int u = 0; u < UG; ++u) {
-      okc[u] = ok[u];
-      if (ok[u]) {
-        raw_float(kr[u], k8[u]);
-        raw_float(vr[u], v8[u]);
-      }
-    }
-    if (bi + 1 < nbatch) { CKV_ISSUE(bi + 1) }
-#pragma unroll
-    for (int u = 0; u < UG; ++u) {
-      if (okc[u]) {  // uniform across the row's lanes
-        float dot[G];
-        dot8<G>(qv, k8[u], dot);
-#pragma unroll
-        for (int j = 0; j < G; ++j) online_add<G>(m, l, acc, j, group_sum<LPR>(dot[j]) * s.tau, 1.f, v8[u]);
-      }
-    }
-  }
-#undef CKV_ISSUE
-  combine_online<D, G, RS>(m, l, acc, part, slot, L.st, L.acc);
   if (slot == PST) return;  // dense: no compensation slot
 
 #pragma unroll
@@ -812,14 +1032,6 @@ __device__ void merge_role(const Shape& s, const StepIO& io, const Work& w, int 
 // splits' partials (the dense mode of merge_role).
 // ---------------------------------------------------------------------------
 template <int D, int G>
-struct DenseCfg {
-  static constexpr int CPL = G == 8 ? 8 : 16;   // channels per lane
-  static constexpr int LPT = D / CPL;           // lanes per token row: 4, 8 or 16
-  static constexpr int TPW = 64 / LPT;          // token rows per wave pass
-  static constexpr int RPP = kBlockSize / TPW;  // rows per lane per page
-  static constexpr int NR = CPL / 8;            // eight-element loads per row
-};
-template <int D, int G>
 struct DenseLds {
   int pg[kDensePages];
   int n[kDensePages];
@@ -829,159 +1041,14 @@ struct DenseLds {
   } u;
 };
 
-__device__ __forceinline__ uint32_t dpp_row_half_mirror(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t dpp_row_mirror(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
-}
-// Sum over each group of LPT consecutive lanes (LPT = 4, 8, 16); every lane
-// of a group receives the same value.
-template <int LPT>
-__device__ __forceinline__ float token_row_sum(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = OpFadd{}(u, dpp_quad_xor1(u));
-  u = OpFadd{}(u, dpp_quad_xor2(u));
-  if (LPT >= 8) u = OpFadd{}(u, dpp_row_half_mirror(u));
-  if (LPT >= 16) u = OpFadd{}(u, dpp_row_mirror(u));
-  return __uint_as_float(u);
-}
-// Reduction over the lanes that hold the same channels (lane % LPT) in the
-// wave's 64 / LPT token slots.
-template <int LPT, class Op>
-__device__ __forceinline__ uint32_t token_slot_reduce(uint32_t x, Op op) {
-  if (LPT == 4) x = op(x, dpp_row_ror4(x));
-  if (LPT <= 8) x = op(x, dpp_row_ror8(x));
-  return across_rows(x, op);
-}
-__device__ __forceinline__ float exp2_from(float a, float m) {  // 2^(a - m), 0 for a = -inf
-  return a == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(a - m);
-}
-
-template <typename KV, int D, int G>
-__device__ __forceinline__ void dense_issue(const Shape& s, const KV* kc, const KV* vc, int g, int pg, int n,
-                                            int ts, int c, Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
-                                            Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
-                                            bool (&ok)[DenseCfg<D, G>::RPP]) {
-  using C = DenseCfg<D, G>;
-#pragma unroll
-  for (int r = 0; r < C::RPP; ++r) {
-    const int tok = r * C::TPW + ts;
-    ok[r] = pg >= 0 && tok < n;
-    if (ok[r]) {
-      const size_t off = (((size_t)pg * s.Hkv + g) * s.bs + tok) * D + c * C::CPL;
-#pragma unroll
-      for (int u = 0; u < C::NR; ++u) {
-        raw_load(kc + off + 8 * u, kr[r][u]);
-        raw_load(vc + off + 8 * u, vr[r][u]);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < C::NR; ++u) {
-        raw_zero(kr[r][u]);
-        raw_zero(vr[r][u]);
-      }
-    }
-  }
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-__device__ __forceinline__ uint32_t raw_word(const Raw8<uint16_t>& r, int i) {
-  return i == 0 ? r.a.x : i == 1 ? r.a.y : i == 2 ? r.a.z : r.a.w;
-}
-
-// qv: the G query rows' CPL channels as float (f32 caches); qp: the same as
-// bf16 pairs (bf16 caches, whose logits use the two-term bf16 dot product).
-template <typename KV, int D, int G>
-__device__ __forceinline__ void dense_page(const float (&qv)[G][DenseCfg<D, G>::CPL],
-                                           const uint32_t (&qp)[G][DenseCfg<D, G>::CPL / 2], float tl,
-                                           const Raw8<KV> (&kr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
-                                           const Raw8<KV> (&vr)[DenseCfg<D, G>::RPP][DenseCfg<D, G>::NR],
-                                           const bool (&ok)[DenseCfg<D, G>::RPP], float (&m)[G], float (&l)[G],
-                                           float (&acc)[G][DenseCfg<D, G>::CPL]) {
-  using C = DenseCfg<D, G>;
-  constexpr int CPL = C::CPL, RPP = C::RPP;
-  float sc[RPP][G];
-#pragma unroll
-  for (int r = 0; r < RPP; ++r) {
-    float dd[G];
-    if constexpr (sizeof(KV) == 2) {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float d = 0.f;
-#pragma unroll
-        for (int u = 0; u < C::NR; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d = dot2_bf16(raw_word(kr[r][u], i), qp[j][4 * u + i], d);
-        dd[j] = d;
-      }
-    } else {
-      float kf[CPL];
-#pragma unroll
-      for (int u = 0; u < C::NR; ++u) raw_float(kr[r][u], *reinterpret_cast<float(*)[8]>(kf + 8 * u));
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) d = fmaf(qv[j][e], kf[e], d);
-        dd[j] = d;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float d = token_row_sum<C::LPT>(dd[j]);
-      sc[r][j] = ok[r] ? d * tl : -INFINITY;
-    }
-  }
-  float p[RPP][G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float mx = sc[0][j];
-#pragma unroll
-    for (int r = 1; r < RPP; ++r) mx = fmaxf(mx, sc[r][j]);
-    if (__ballot(mx > m[j]) != 0) {  // uniform over the wave
-      const float mn = fmaxf(m[j], mx);
-      const float f = exp2_from(m[j], mn);
-      l[j] *= f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) acc[j][e] *= f;
-      m[j] = mn;
-    }
-#pragma unroll
-    for (int r = 0; r < RPP; ++r) {
-      p[r][j] = ok[r] ? __builtin_amdgcn_exp2f(sc[r][j] - m[j]) : 0.f;
-      l[j] += p[r][j];
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < RPP; ++r) {
-    float vf[CPL];
-#pragma unroll
-    for (int u = 0; u < C::NR; ++u) raw_float(vr[r][u], *reinterpret_cast<float(*)[8]>(vf + 8 * u));
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) acc[j][e] = fmaf(p[r][j], vf[e], acc[j][e]);
-  }
-}
-
 template <typename KV, int D, int G>
 __global__ __launch_bounds__(kThreads, 2) void dense_kernel(Shape s, StepIO io, Work w) {
-  using C = DenseCfg<D, G>;
-  constexpr int CPL = C::CPL, LPT = C::LPT, RPP = C::RPP, NR = C::NR, PST = kPartStride(D);
-  constexpr int NW = kThreads / 64;
-  // bf16 pages are double-buffered in registers up to G = 4; otherwise pages
-  // are loaded one at a time
-  constexpr bool kPrefetch = sizeof(KV) == 2 && G <= 4;
+  constexpr int PST = kPartStride(D);
   __shared__ DenseLds<D, G> L;
   __shared__ uint32_t slot;
   const int t = (int)blockIdx.x, split = t % s.n_splits, bg = t / s.n_splits;
   const int b = bg / s.Hkv, g = bg % s.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane % LPT, ts = lane / LPT;
+  const int tid = threadIdx.x;
   const int Lseq = clamp_len(io.seq_lens[b], s.max_blocks * s.bs);
   const int M = (Lseq + s.bs - 1) / s.bs;
   const int first = split * s.pages_per_split;
@@ -995,104 +1062,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_kernel(Shape s, StepIO io, 
     L.pg[e] = p;
     L.n[e] = n;
   }
-  const KV* q = static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D + c * CPL;
-  float qv[G][CPL];
-  uint32_t qp[G][CPL / 2];
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-#pragma unroll
-    for (int u = 0; u < NR; ++u) {
-      if constexpr (sizeof(KV) == 2) {
-        Raw8<KV> rq;
-        raw_load(q + (size_t)j * D + 8 * u, rq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qp[j][4 * u + i] = raw_word(rq, i);
-      } else {
-        load8(q + (size_t)j * D + 8 * u, *reinterpret_cast<float(*)[8]>(&qv[j][8 * u]));
-      }
-    }
-  const float tl = s.tau * 1.44269504088896340736f;  // logits in log2 units
-  float m[G], l[G], acc[G][CPL];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[j][e] = 0.f;
-  }
   __syncthreads();
-
-  const KV* kc = static_cast<const KV*>(io.k_cache);
-  const KV* vc = static_cast<const KV*>(io.v_cache);
-  const int np = nb > wave ? (nb - 1 - wave) / NW + 1 : 0;  // this wave's pages: wave + NW i
-  Raw8<KV> ka[RPP][NR], va[RPP][NR];
-  bool oka[RPP];
-  if constexpr (kPrefetch) {
-    Raw8<KV> kb[RPP][NR], vb[RPP][NR];
-    bool okb[RPP];
-    if (np > 0) dense_issue<KV, D, G>(s, kc, vc, g, L.pg[wave], L.n[wave], ts, c, ka, va, oka);
-    for (int pi = 0; pi < np; pi += 2) {
-      if (pi + 1 < np) {
-        const int bl = wave + NW * (pi + 1);
-        dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, kb, vb, okb);
-      }
-      dense_page<KV, D, G>(qv, qp, tl, ka, va, oka, m, l, acc);
-      if (pi + 1 < np) {
-        if (pi + 2 < np) {
-          const int bl = wave + NW * (pi + 2);
-          dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, ka, va, oka);
-        }
-        dense_page<KV, D, G>(qv, qp, tl, kb, vb, okb, m, l, acc);
-      }
-    }
-  } else {
-    for (int pi = 0; pi < np; ++pi) {
-      const int bl = wave + NW * pi;
-      dense_issue<KV, D, G>(s, kc, vc, g, L.pg[bl], L.n[bl], ts, c, ka, va, oka);
-      dense_page<KV, D, G>(qv, qp, tl, ka, va, oka, m, l, acc);
-    }
-  }
-
-  // combine the token slots of the wave, then the waves, into one partial
-  // per head: [max (natural log units), sum, -, -, acc[D]]
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float mw = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(m[j]), OpFmax{}));
-    const float f = exp2_from(m[j], mw);
-    const float lw = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(l[j] * f), OpFadd{}));
-    float a[CPL];
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) a[e] = __uint_as_float(token_slot_reduce<LPT>(__float_as_uint(acc[j][e] * f), OpFadd{}));
-    if (lane < LPT) {
-      float* rw = L.u.red[wave][j];
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) rw[4 + c * CPL + e] = a[e];
-      if (c == 0) {
-        rw[0] = mw;
-        rw[1] = lw;
-      }
-    }
-  }
-  __syncthreads();
-  const Coh part(w.gpart + ((size_t)bg * s.n_splits + split) * G * PST, (size_t)G * PST * 4);
-  for (int o = tid; o < G * D; o += kThreads) {
-    const int j = o / D, d = o % D;
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) Mx = fmaxf(Mx, L.u.red[v][j][0]);
-    float a = 0.f, ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const float f = exp2_from(L.u.red[v][j][0], Mx);
-      a = fmaf(L.u.red[v][j][4 + d], f, a);
-      ls = fmaf(L.u.red[v][j][1], f, ls);
-    }
-    part.put(j * PST + 4 + d, a);
-    if (d == 0) {
-      part.put(j * PST, Mx * 0.69314718055994530942f);  // -inf stays -inf
-      part.put(j * PST + 1, ls);
-    }
-  }
+  dense_span<KV, D, G>(s, io, b, g, L.pg, L.n, nb, L.u.red,
+                      w.gpart + ((size_t)bg * s.n_splits + split) * G * PST, PST);
   const uint32_t prev = arrive(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + 2, &slot);
   if (prev == (uint32_t)(s.n_splits - 1)) merge_role<D, G, kModeDense>(s, io, w, bg, L.u.merge);
 }
