@@ -14,11 +14,11 @@
  *   2. ckv_score_select: score every block from its summary with the
  *      practical residual criterion - a second-order attention-mass estimate
  *      times the estimated within-block logit variance - and keep the top-k
- *      blocks under a token budget.  CompKV abstract (shd-paper.top listing):
- *      the residual left by block-level mean compensation is governed by
- *      block attention mass and within-block logit variation, approximated
- *      from compact block statistics; review "Summary", paper Section 3,
- *      Eqs. 4-7.
+ *      blocks under a token budget.  CompKV abstract (shd-paper.top
+ *      listing): the error a block leaves behind under mean compensation
+ *      depends on the attention it draws and on how far its logits spread,
+ *      and small per-block statistics estimate it; review "Summary", paper
+ *      Section 3, Eqs. 4-7.
  *   3. ckv_compensated_decode_attention: exact attention over the selected
  *      blocks' tokens; every omitted block enters the softmax once, with its
  *      block-mean logit, weighted by its token count, carrying its mean

@@ -9,18 +9,19 @@ common, and they hold none of the method's arithmetic).
 What is computed, and where it is described (pages cited by title/section):
 
 * [abstract] "CompKV: Compensation-Aware KV Selection for Long-Context LLM
-  Inference", shd-paper.top listing, original English abstract: tokens are
-  divided into blocks; exact attention is computed over a selected subset;
-  the omitted tail gets coarse compensation; the residual left by block-level
-  mean compensation is governed by block attention mass and within-block
-  logit variation; compact block statistics approximate it and give the
-  selection criterion.
-* [review] evolve.pub review of the same paper, "Summary": under Mean
-  compensation an omitted block contributes its block-mean logit; exact KL
-  identity; residual jointly governed by attention mass and within-block
-  logit variance (paper Section 3, Eqs. 4-7); blocks are scored from mean
-  key, grouped key variance (default r = 4) and mean value, with a
-  second-order mass estimate.
+  Inference", shd-paper.top listing, original English abstract: the context
+  is cut into blocks, a chosen subset is attended exactly and the rest gets a
+  coarse correction; the authors tie the error that the block-mean correction
+  leaves to two quantities, the attention the block draws and the spread of
+  its logits, and estimate that error from small per-block statistics to rank
+  the blocks.
+* [review] evolve.pub review of the same paper, "Summary": with Mean
+  compensation each omitted block stands in with the logit of its mean; an
+  exact KL identity holds; how much an omitted block leaves unexplained
+  depends on both its attention mass and the variance of its logits (paper
+  Section 3, Eqs. 4-7); scores come from the mean key, the key variance in
+  r channel groups (4 by default) and the mean value, with a mass estimate
+  taken to second order.
 * [review FAQ] 2d + r + 1 scalars per block, updated incrementally as tokens
   enter the cache.
 * [review Strengths] App. A.1 exact log-partition KL identity; A.2-A.3
@@ -49,10 +50,15 @@ their verbal statements.  Readings taken where they are silent:
   R9  "updated incrementally" = the tail block's summary is recomputed from
       its raw tokens when a token is appended.
 
-Parity unpinned (the pages print no value that fixes them): the functional
-form of the practical score (R5), the GQA aggregation (R6) and the grouping
-layout (R2).  Their small-variance limits and special cases are pinned by
-the tests.
+The pages print no value for the readings R2, R5 and R6.  Each is pinned
+where the mathematics fixes it (tests/test_oracle_pins.py): the grouped
+estimate (R2, R3) is exact when a block's key deviations are uncorrelated
+with equal variance inside each group, and reduces to closed forms at r = 1
+and r = d; the practical score (R5) and its GQA group sum (R6) converge, head
+by head and summed over the group, to the exact per-head normalised residual
+as the blocks' spread shrinks, and the group selection then equals the
+brute-force minimiser of the summed KL over every k-subset.  Beyond second
+order in the spread, the form of R5 is a reading, not a derived fact.
 """
 from __future__ import annotations
 
@@ -134,13 +140,9 @@ def summarize_block(k_blk: np.ndarray, v_blk: np.ndarray, r: int, kv_dtype: str)
     n, H, d = k_blk.shape
     if d % r:
         raise ValueError("r must divide head_dim")
-    # Means are taken on data shifted by the block's first token, so a block
-    # whose tokens are all equal gets exactly that token as its mean and
-    # exactly zero variance (for bf16 inputs the shifted sums are exact in
-    # float64; only the division by n rounds).
-    mu = k_blk[0] + (k_blk - k_blk[0][None]).sum(axis=0) / n   # mean key per channel
-    nu = v_blk[0] + (v_blk - v_blk[0][None]).sum(axis=0) / n   # mean value per channel
-    var = ((k_blk - mu[None]) ** 2).sum(axis=0) / n            # population variance per channel
+    mu = k_blk.sum(axis=0) / n                          # mean key per channel
+    nu = v_blk.sum(axis=0) / n                          # mean value per channel
+    var = ((k_blk - mu[None]) ** 2).sum(axis=0) / n     # population variance per channel
     gvar = var.reshape(H, r, d // r).mean(axis=2)      # mean over each channel group (R2, R3)
     return (round_storage(mu, kv_dtype), round_storage(nu, kv_dtype),
             round_storage(gvar, "f32"), n)

@@ -397,7 +397,9 @@ def test_constant_key_blocks_make_compensation_exact():
     rng = np.random.default_rng(31)
     d, b, M, Hq, Hkv = 8, 4, 9, 4, 2
     q = rng.standard_normal((Hq, d))
-    keys = rng.standard_normal((M, Hkv, d))
+    # float32-representable keys (as the caches hold): a block's sum of equal
+    # rows is exact in float64, so its mean is that row exactly
+    keys = rng.standard_normal((M, Hkv, d)).astype(np.float32).astype(np.float64)
     k = np.repeat(keys, b, axis=0)[: M * b - 1]          # ragged tail block
     v = rng.standard_normal((M * b - 1, Hkv, d))
     summ = O.build_summaries(k, v, b, 4, "f64")
@@ -501,3 +503,146 @@ def test_hand_worked_example():
     Z = math.exp(log_z[0])
     np.testing.assert_allclose(resid[0] * Z, [0, e + 1 / e - 2], atol=1e-14)
     np.testing.assert_allclose(mass[0] * Z, [2 * e15, e + 1 / e], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Widening of stored values, grouped-variance layout, and the GQA aggregation
+# ---------------------------------------------------------------------------
+
+
+def test_widen_bf16_matches_torch_for_every_bit_pattern():
+    # Every one of the 65536 bf16 bit patterns (zeros, subnormals, infinities,
+    # both signs) widens to the value torch gives it; NaNs stay NaN.
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):   # signalling NaN patterns
+        got = O.widen(bits, "bf16")
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127                 # exponent all ones, nonzero fraction, two signs
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.signbit(got[0x8000]) and got[0x8000] == 0.0
+    f = np.random.default_rng(1).standard_normal(1000).astype(np.float32)
+    np.testing.assert_array_equal(O.widen(f, "f32"), torch.from_numpy(f).to(torch.float64).numpy())
+
+
+@pytest.mark.parametrize("r", [2, 4])
+def test_grouped_variance_exact_for_uncorrelated_group_constant_deviations(r):
+    # If a block's key deviations are uncorrelated across channels and have
+    # one variance a_t^2 inside each channel group t, the within-block logit
+    # variance tau^2 q^T C q is exactly tau^2 sum_t |q_{C_t}|^2 a_t^2, which is
+    # what the grouped estimate gives with contiguous groups.  Rows of a
+    # Hadamard matrix (zero mean, mutually orthogonal) make the sample
+    # covariance exactly diagonal.
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(50 + r)
+    d, b = 8, 16
+    Hm = hadamard(16).astype(np.float64)
+    q = rng.standard_normal((1, d))
+    a = rng.uniform(0.2, 1.5, size=r)
+    base = rng.standard_normal(d)
+    dev = np.stack([a[c // (d // r)] * Hm[1 + c] for c in range(d)], axis=1)   # [b, d]
+    k = (base[None] + dev)[:, None, :]
+    summ = O.build_summaries(k, k, b, r, "f64")
+    sc = O.block_scores(q, summ, r)
+    exact = np.var(token_logits(q, k, 0, 1))
+    assert sc.var_hat[0, 0] == pytest.approx(exact, rel=1e-6)     # gvar is stored in f32
+    # teeth: interleaved groups (channel c in group c mod r) would not be exact
+    gv_inter = np.array([np.mean([a[c // (d // r)] ** 2 for c in range(t, d, r)]) for t in range(r)])
+    qn_inter = np.array([(q[0, t::r] ** 2).sum() for t in range(r)])
+    assert abs((qn_inter @ gv_inter) / d - exact) > 1e-3 * exact
+
+
+def _exact_head_residuals(q, k, h, G, b):
+    """Per block, the exact residual R of Mean compensation over the head's
+    partition function Z, from the token logits (independent of the oracle):
+    R_i = sum_{j in i} e^{s_j} - n_i e^{mean_j s_j}."""
+    s = token_logits(q, k, h, G)
+    L = s.shape[0]
+    M = -(-L // b)
+    e = np.exp(s)
+    Z = e.sum()
+    R = np.array([e[i * b:(i + 1) * b].sum() - min(b, L - i * b) * math.exp(s[i * b:(i + 1) * b].mean())
+                  for i in range(M)])
+    return R / Z
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_group_score_limit_is_the_exact_group_residual(G):
+    # Each head's KL under Mean compensation is -log(1 - sum_omitted R_h/Z_h)
+    # (review "Strengths", App. A.1), so to first order a block matters to
+    # the KV head's query heads through sum_h R_h/Z_h, each head normalised
+    # by its own partition function.  With r = d and one varying channel
+    # per block the variance estimate is exact, and as the blocks' spread
+    # shrinks each head's S_h/Z_hat_h and the group score must approach the
+    # exact normalised residuals.  The heads' logit scales differ by 10x, so
+    # normalising by a shared Z would not converge.
+    rng = np.random.default_rng(700 + G)
+    d, b, M, Hkv = 8, 16, 6, 2
+    Hq = G * Hkv
+    scales = np.geomspace(0.3, 3.0, G)
+    q = rng.standard_normal((Hq, d)) * np.tile(scales, Hkv)[:, None]
+    base = rng.standard_normal((M, Hkv, d))
+    eta = np.zeros((M, b, Hkv, d))
+    for i in range(M):
+        for g in range(Hkv):
+            eta[i, :, g, (i + 2 * g) % d] = rng.standard_normal(b)
+    prev_h = prev_g = None
+    for eps in (1e-1, 1e-2, 1e-3):
+        k = (base[:, None] + eps * eta).reshape(M * b, Hkv, d)
+        summ = O.build_summaries(k, k, b, d, "f64")
+        sc = O.block_scores(q, summ, d)
+        rho = np.zeros((Hkv, M))
+        dev_h = 0.0
+        for h in range(Hq):
+            rh = _exact_head_residuals(q, k, h, G, b)
+            dev_h = max(dev_h, float(np.abs(sc.head_score[h] / rh - 1).max()))
+            rho[h // G] += rh
+        dev_g = float(np.abs(sc.group_score / rho - 1).max())
+        if prev_h is not None:
+            assert dev_h < prev_h / 5 and dev_g < prev_g / 5      # converges with eps
+        prev_h, prev_g = dev_h, dev_g
+        # teeth: one Z_hat shared by the group's heads misses the exact sum
+        z_hat = np.exp(sc.log_z_hat)
+        raw = sc.head_score * z_hat[:, None]
+        shared = np.stack([raw[g * G:(g + 1) * G].sum(0) / z_hat[g * G:(g + 1) * G].sum() for g in range(Hkv)])
+        assert np.abs(shared / rho - 1).max() > 0.1
+    assert dev_h < 5e-3 and dev_g < 5e-3
+
+
+def test_brute_force_min_group_kl_is_group_score_topk():
+    # Two query heads share a KV head and one selection.  Over every k-subset,
+    # the subset with the smallest summed KL(p_hat_h || p_h) of the two heads
+    # (token-level distributions) is the top-k of the exact group residual
+    # sum_h R_h/Z_h, and, with exact variance estimates and small spreads,
+    # the oracle's CompKV selection (review "Summary"; "Strengths" App. A.1).
+    # The heads' logit scales differ by 5x: ranking by the unnormalised sum
+    # of the heads' scores misses the best subset in some of the cases.
+    d, b, M, kk, G = 8, 4, 8, 3, 2
+    unnormalised_misses = 0
+    for seed in range(12):
+        rng = np.random.default_rng(800 + seed)
+        q = rng.standard_normal((G, d)) * np.array([[0.5], [2.5]])
+        base = rng.standard_normal((M, 1, d))
+        k = np.repeat(base, b, axis=0).copy()
+        for i in range(M):
+            k[i * b:(i + 1) * b, 0, i % d] += rng.uniform(0.02, 0.4) * rng.standard_normal(b)
+        v = rng.standard_normal((M * b, 1, d))
+        summ = O.build_summaries(k, v, b, d, "f64")
+        p = [softmax(token_logits(q, k, h, G)) for h in range(G)]
+        kls = {}
+        for sub in itertools.combinations(range(M), kk):
+            kls[sub] = sum(O.kl_divergence(compensated_token_distribution(q, k, h, G, set(sub), b)[0], p[h])
+                           for h in range(G))
+        ranked = sorted(kls.items(), key=lambda t: t[1])
+        best = ranked[0][0]
+        assert ranked[1][1] - ranked[0][1] > 1e-3 * ranked[0][1], seed
+        rho = sum(_exact_head_residuals(q, k, h, G, b) for h in range(G))
+        assert tuple(sorted(np.argsort(-rho)[:kk])) == best, seed
+        for mode in ("residual_exact", "compkv"):
+            res = O.decode_step(q, k, v, summ, budget_tokens=kk * b, block_size=b, r=d, score_mode=mode)
+            assert tuple(res.selected[0]) == best, (seed, mode)
+        sc = O.block_scores(q, summ, d)
+        raw = (sc.head_score * np.exp(sc.log_z_hat)[:, None]).sum(axis=0)
+        unnormalised_misses += tuple(sorted(np.argsort(-raw)[:kk])) != best
+    assert unnormalised_misses >= 2
