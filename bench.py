@@ -114,6 +114,122 @@ def graph_time_us(torch, fn, n: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+# ---- CPU baseline: the oracle on the host's cores ---------------------------
+
+_ORACLE_JOB = {}
+
+
+def _oracle_one_kv_head(g: int) -> float:
+    """One decode step of KV head g (and its query heads) in the oracle; the
+    heads are independent, so the KV heads of a step can run side by side."""
+    from oracle import compkv_oracle as O
+    j = _ORACLE_JOB
+    G = j["G"]
+    sub = O.Summaries(j["summ"].mean_k[:, g:g + 1], j["summ"].mean_v[:, g:g + 1], j["summ"].gvar[:, g:g + 1],
+                      j["summ"].count)
+    res = O.decode_step(j["q"][g * G:(g + 1) * G], j["k"][:, g:g + 1], j["v"][:, g:g + 1], sub,
+                        budget_tokens=j["budget"], block_size=j["bs"], r=j["r"])
+    return float(res.out.sum())
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_oracle_baseline(w, runs: int = 5) -> dict:
+    """The CPU oracle's decode step on the same layer, summaries prebuilt:
+    the median of `runs` steps on one core (one process, one BLAS thread),
+    and the median of `runs` steps on the host's cores (one process per KV
+    head, up to the cores this process may use, each with one BLAS thread).
+    Runs before anything touches the GPU (the worker processes are forked)."""
+    import multiprocessing as mp
+    import statistics
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import compkv_oracle as O
+    q, k, v = O.sequence_arrays(w.q[0], w.k_tokens[0], w.v_tokens[0], w.dtype)
+    t0 = time.perf_counter()
+    summ = O.build_summaries(k, v, w.block_size, w.r_groups, w.dtype)
+    build_s = time.perf_counter() - t0
+    _ORACLE_JOB.update(q=q, k=k, v=v, summ=summ, G=w.num_q_heads // w.num_kv_heads, budget=w.budget_tokens,
+                       bs=w.block_size, r=w.r_groups)
+    H = w.num_kv_heads
+    one = []
+    with threadpool_limits(limits=1):
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            O.decode_step(q, k, v, summ, budget_tokens=w.budget_tokens, block_size=w.block_size, r=w.r_groups)
+            one.append(time.perf_counter() - t0)
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    workers = max(1, min(H, avail, 16))
+    many = []
+    with threadpool_limits(limits=1):
+        with mp.get_context("fork").Pool(workers) as pool:
+            pool.map(_oracle_one_kv_head, range(H))  # warm the workers
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                pool.map(_oracle_one_kv_head, range(H))
+                many.append(time.perf_counter() - t0)
+    _ORACLE_JOB.clear()
+    med_one, med_many = statistics.median(one), statistics.median(many)
+    return {"value": round(med_many * 1e6, 1), "unit": "us/step", "cores": workers, "kind": "oracle",
+            "sample": (f"median of {runs} float64 numpy oracle decode steps of the same {int(w.seq_lens[0])}-token "
+                       f"layer, summaries prebuilt ({build_s:.1f} s), {workers} processes of one BLAS thread "
+                       f"each taking a KV head; host CPU"),
+            "one_core_us": round(med_one * 1e6, 1), "one_core_runs_us": [round(x * 1e6) for x in one],
+            "all_cores_runs_us": [round(x * 1e6) for x in many], "nproc": os.cpu_count(),
+            "usable_cpus": avail, "cpu_model": cpu_model()}
+
+
+# ---- GPU timing --------------------------------------------------------------
+
+
+def replays_for(steps: int, want: int = 10) -> int:
+    """The largest replay count <= want that divides `steps`."""
+    for r in range(min(want, steps), 0, -1):
+        if steps % r == 0:
+            return r
+    return 1
+
+
+def timed_replays(torch, fn, steps: int, replays: int):
+    """Capture steps // replays consecutive steps fn(0), fn(1), ... into one
+    HIP graph, replay it `replays` times back to back with an event between
+    replays (on the capturing stream), and return (us per step over all
+    `steps`, per-replay us per step)."""
+    per = steps // replays
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per):
+            fn(i)
+    g.replay()  # untimed: the first replay uploads the graph
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for r in range(replays):
+        g.replay()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    samples = [ev[r].elapsed_time(ev[r + 1]) * 1e3 / per for r in range(replays)]
+    total = ev[0].elapsed_time(ev[replays]) * 1e3 / (per * replays)
+    return total, samples
+
+
+def distribution(samples) -> dict:
+    import numpy as np
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "samples": len(a)}
+
+
 def sweep(args, dev0) -> int:
     """Step latency over context lengths and budgets: 32K, 64K, 128K tokens x
     512, 1024, 2048-token budgets (the CompKV review's length/budget grid is
@@ -221,16 +337,15 @@ def sweep_r(args, dev0) -> int:
     return 0
 
 
-def decode_loop(args, dev0) -> int:
+def decode_loop_result(args, dev0, n_layers: int) -> dict:
     """Prefill plus a generation loop at 128K context (Llama-3.1-8B layer
     shape): the bulk summary build over 131072 tokens, then 64 decode steps,
     each appending one token (written into its page and the tail block's
     summary refreshed) and running the step with a 2048-token budget, in one
     ckv_decode_step_append call (with --loop-two-launch: ckv_append_tokens,
-    then ckv_decode_step).  The
-    steps of all layer copies are captured into one HIP graph and replayed;
-    a step visits every layer copy in turn, as a model's layer loop would, so
-    summaries come from HBM."""
+    then ckv_decode_step).  The steps of all layer copies are captured into
+    one HIP graph and replayed; a step visits every layer copy in turn, as a
+    model's layer loop would, so summaries come from HBM."""
     import numpy as np
     import torch
     from compensated_kv_selection_amd import compkv as C
@@ -245,7 +360,7 @@ def decode_loop(args, dev0) -> int:
     base = to_device(w, dev0, k_cache=kc, v_cache=vc)
     del kc, vc
     dims = base.dims
-    n_layers = max(1, args.loop_layers)
+    n_layers = max(1, n_layers)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     loops, build_ms = [], []
     for li in range(n_layers):
@@ -269,6 +384,8 @@ def decode_loop(args, dev0) -> int:
 
     run_all()  # eager pass
     torch.cuda.synchronize()
+    for lp in loops:
+        C.workspace_status(lp.ws)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run_all()
@@ -278,20 +395,87 @@ def decode_loop(args, dev0) -> int:
     g.replay()
     ev[1].record()
     torch.cuda.synchronize()
+    for lp in loops:
+        C.workspace_status(lp.ws)
     us = ev[0].elapsed_time(ev[1]) * 1e3 / (n_steps * n_layers)
-    print(json.dumps({"decode_loop": "prefill + 64 appending decode steps, graph replay",
-                      "seq_len_start": int(w.seq_lens[0]), "steps": n_steps,
-                      "budget_tokens": w.budget_tokens, "layer_copies": n_layers,
-                      "prefill_build_us": round(float(np.median(build_ms)) * 1e3, 1),
-                      "us_per_layer_step": round(us, 2),
-                      "per_layer_step": ("ckv_append_tokens (new key and value into their page, "
-                                         "tail-block summary), then ckv_decode_step" if args.loop_two_launch
-                                         else "ckv_decode_step_append (append and step)"),
-                      "launches_per_layer_step": (1 + C.decode_step_launches(dims, w.budget_tokens)
-                                                  if args.loop_two_launch
-                                                  else C.decode_step_append_launches(dims, w.budget_tokens)),
-                      "data": "synthetic"}), flush=True)
+    M = -(-(int(w.seq_lens[0]) + n_steps) // 16)
+    ab = algorithmic_bytes(M, 8, 128, 4, min(M, w.budget_tokens // 16), 16, 2)
+    res = {"decode_loop": "prefill + 64 appending decode steps, graph replay",
+           "seq_len_start": int(w.seq_lens[0]), "steps": n_steps,
+           "budget_tokens": w.budget_tokens, "layer_copies": n_layers,
+           "prefill_build_us": round(float(np.median(build_ms)) * 1e3, 1),
+           "us_per_layer_step": round(us, 2),
+           "step_algorithmic_bytes": ab["total"],
+           "step_effective_GBps": round(ab["total"] / (us * 1e-6) / 1e9, 1),
+           "per_layer_step": ("ckv_append_tokens (new key and value into their page, "
+                              "tail-block summary), then ckv_decode_step" if args.loop_two_launch
+                              else "ckv_decode_step_append (append and step)"),
+           "launches_per_layer_step": (1 + C.decode_step_launches(dims, w.budget_tokens)
+                                       if args.loop_two_launch
+                                       else C.decode_step_append_launches(dims, w.budget_tokens)),
+           "data": "synthetic"}
+    del loops, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_loop(args, dev0) -> int:
+    print(json.dumps(decode_loop_result(args, dev0, args.loop_layers)), flush=True)
     return 0
+
+
+def batched_result(args, dev0, n_layers: int, w=None) -> dict:
+    """The batched ragged decode step: 16 sequences of 16K to 64K tokens
+    (Hq 32, Hkv 8, d 128, bf16, paged), 1024-token budget, steps rotating
+    over layer copies, graph replay."""
+    import torch
+    from compensated_kv_selection_amd import compkv as C
+    from compensated_kv_selection_amd import workloads as W
+    from compensated_kv_selection_amd.tensors import to_device
+    w = w if w is not None else W.make_preset("batched_ragged", seed=args.seed)
+    base = to_device(w, dev0)
+    dims = base.dims
+    layers = []
+    for li in range(n_layers):
+        kc = base.k_cache if li == 0 else base.k_cache.clone()
+        vc = base.v_cache if li == 0 else base.v_cache.clone()
+        summ = C.allocate_summaries(dims, dev0)
+        C.build_summaries(dims, kc, vc, base.block_table, base.seq_lens, summ)
+        layers.append((kc, vc, summ))
+    budget = w.budget_tokens
+    ws = C.allocate_workspace(C.workspace_bytes(dims, budget), dev0)
+    kmax = max(1, dims.kmax(budget))
+    sel = torch.empty((dims.batch, dims.num_kv_heads, kmax), dtype=torch.int32, device=dev0)
+    nsel = torch.empty((dims.batch, dims.num_kv_heads), dtype=torch.int32, device=dev0)
+    out = torch.empty((dims.batch, dims.num_q_heads, dims.head_dim), dtype=torch.float32, device=dev0)
+    lse = torch.empty((dims.batch, dims.num_q_heads), dtype=torch.float32, device=dev0)
+
+    def step(i):
+        kc, vc, summ = layers[i % n_layers]
+        C.decode_step(dims, base.q, kc, vc, summ, base.block_table, base.seq_lens, budget, ws,
+                      selected=sel, num_selected=nsel, out=out, lse=lse)
+
+    for i in range(4):
+        step(i)
+    torch.cuda.synchronize()
+    us, samples = timed_replays(torch, step, 40, 10)
+    C.workspace_status(ws)
+    ab = {"total": 0}
+    for Lb in w.seq_lens:
+        Mb = -(-int(Lb) // 16)
+        ab["total"] += algorithmic_bytes(Mb, w.num_kv_heads, w.head_dim, w.r_groups,
+                                         min(Mb, budget // 16), 16, 2)["total"]
+    res = {"workload": (f"batched_ragged: {w.batch} sequences of {int(w.seq_lens.min())} to "
+                        f"{int(w.seq_lens.max())} tokens ({int(w.seq_lens.sum())} in all), Hq {w.num_q_heads}, "
+                        f"Hkv {w.num_kv_heads}, d {w.head_dim}, budget {budget} tokens, {n_layers} rotating "
+                        f"layer buffers"),
+           "us_per_step": round(us, 2), "distribution_us": distribution(samples),
+           "algorithmic_bytes": ab["total"], "effective_GBps": round(ab["total"] / (us * 1e-6) / 1e9, 1),
+           "pct_hbm_peak": round(100 * ab["total"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+           "launches": C.decode_step_launches(dims, budget), "data": "synthetic"}
+    del layers, base
+    torch.cuda.empty_cache()
+    return res
 
 
 def main() -> int:
@@ -302,9 +486,11 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=16, help="distinct layer buffers the steps rotate over")
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-steps", type=int, default=20)
+    ap.add_argument("--cpu-runs", type=int, default=5, help="oracle steps per CPU-baseline median")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="leave out the batched ragged step and the 128K decode loop")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain elementwise copy of this many MiB (counter calibration)")
     ap.add_argument("--rocprof-summary", default="",
@@ -340,6 +526,19 @@ def main() -> int:
     from compensated_kv_selection_amd import workloads as W
     from compensated_kv_selection_amd.tensors import to_device
 
+    w = None
+    cpu = None
+    headline = not (args.sweep or args.decode_loop or args.sweep_r or args.copy_mb)
+    if headline:
+        t_gen = time.time()
+        w = W.make_preset(args.workload, seed=args.seed)
+        print(f"[bench] generated {args.workload} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+        if not args.no_cpu and w.batch == 1:
+            # before anything touches the GPU: the oracle's worker processes are forked
+            t0 = time.time()
+            cpu = cpu_oracle_baseline(w, args.cpu_runs)
+            print(f"[bench] CPU oracle baseline in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
@@ -365,9 +564,6 @@ def main() -> int:
         return decode_loop(args, dev0)
     if args.sweep_r:
         return sweep_r(args, dev0)
-    t_gen = time.time()
-    w = W.make_preset(args.workload, seed=args.seed)
-    print(f"[bench] generated {args.workload} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
     base = to_device(w, dev0)
     dims = base.dims
     budget = w.budget_tokens
@@ -409,40 +605,24 @@ def main() -> int:
         C.decode_step(dims, base.q, kc, vc, summ, base.block_table, base.seq_lens, budget, ws,
                       selected=sel, num_selected=nsel, out=out, lse=lse)
 
-    def graph_of(fn, n):
-        """Capture n consecutive steps into one HIP graph (host launch cost
-        leaves the timed region; the kernels run back to back)."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        return g
-
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    graph = graph_of(step, args.steps)
-    graph.replay()  # untimed: first replay uploads the graph
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    C.workspace_status(ws)
+    # The timed region: `steps` steps, as `replays` replays of one HIP graph of
+    # steps / replays consecutive steps, back to back on the launch stream,
+    # with an event between replays; synchronized before and after.
+    replays = replays_for(args.steps)
     t0 = time.perf_counter()
-    ev0.record()
-    graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
+    us_per_step, samples = timed_replays(torch, step, args.steps, replays)
     wall_s = time.perf_counter() - t0
-    region_ms = ev0.elapsed_time(ev1)
-    us_per_step = region_ms * 1e3 / args.steps
-    print(f"[bench] {args.steps} steps (graph replay): {us_per_step:.2f} us/step (events), "
-          f"wall {wall_s * 1e6 / args.steps:.1f} us/step", file=sys.stderr, flush=True)
+    # every bounded wait of the timed steps ended in time (else this raises
+    # and the run fails: the outputs of those steps would be unspecified)
+    C.workspace_status(ws)
+    print(f"[bench] {args.steps} steps ({replays} graph replays): {us_per_step:.2f} us/step (events), "
+          f"wall {wall_s:.2f} s", file=sys.stderr, flush=True)
 
-    # The graph holds `steps` back-to-back launches of the step's kernel(s) on
-    # the current stream; the events bracket its replay on that stream.
-    # With three launches per step the three are timed together.
     launches = C.decode_step_launches(dims, budget)
-    per_launch_us = np.array([us_per_step])
-
-    # summed over the batch's sequences (each with its own block count)
     ab = {"summary": 0, "selected_kv": 0, "total": 0}
     for Lb in w.seq_lens:
         Mb = -(-int(Lb) // w.block_size)
@@ -454,9 +634,10 @@ def main() -> int:
         * 2 * kv_bytes  # every page's keys and values
     tokens_desc = (f"{L} tokens" if w.batch == 1 else
                    f"{int(w.seq_lens.min())} to {L} tokens per sequence ({int(w.seq_lens.sum())} in all)")
-    avg_launch_us = float(per_launch_us.mean())
-    achieved = ab["total"] / (avg_launch_us * 1e-6) / 1e9
-    eff_gbps = ab["total"] / (us_per_step * 1e-6) / 1e9
+    # one launch per step: the per-launch time is the per-step time
+    avg_launch_us = us_per_step / launches
+    achieved = ab["total"] / (us_per_step * 1e-6) / 1e9
+    eff_gbps = achieved
 
     dense = None
     if not args.no_dense:
@@ -469,38 +650,15 @@ def main() -> int:
             C.dense_decode_attention(dims, base.q, kc, vc, base.block_table, base.seq_lens, dws,
                                      out=dout, lse=dlse)
 
-        dn = max(16, args.steps // 4)
         for i in range(3):
             dstep(i)
         torch.cuda.synchronize()
-        dgraph = graph_of(dstep, dn)
-        dgraph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dgraph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        dense_us = e0.elapsed_time(e1) * 1e3 / dn
-        dense_bytes = kv_all
-        dense = {"us_per_step": round(dense_us, 2), "bytes": dense_bytes,
-                 "GBps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+        dense_us, dsamples = timed_replays(torch, dstep, 48, 6)
+        C.workspace_status(dws)
+        dense = {"us_per_step": round(dense_us, 2), "distribution_us": distribution(dsamples),
+                 "bytes": kv_all, "GBps": round(kv_all / (dense_us * 1e-6) / 1e9, 1),
+                 "pct_hbm_peak": round(100 * kv_all / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
                  "speedup_of_compkv": round(dense_us / us_per_step, 2)}
-
-    cpu = None
-    if not args.no_cpu:
-        from threadpoolctl import threadpool_limits
-        from oracle import compkv_oracle as O
-        with threadpool_limits(limits=1):
-            q, k, v = O.sequence_arrays(w.q[0], w.k_tokens[0], w.v_tokens[0], w.dtype)
-            osumm = O.build_summaries(k, v, w.block_size, w.r_groups, w.dtype)
-            t0 = time.perf_counter()
-            for _ in range(args.cpu_steps):
-                O.decode_step(q, k, v, osumm, budget_tokens=budget, block_size=w.block_size, r=w.r_groups)
-            cpu_s = (time.perf_counter() - t0) / args.cpu_steps
-        cpu = {"value": round(cpu_s * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
-               "sample": f"{args.cpu_steps} float64 numpy oracle decode steps of the same 128K-token "
-                         f"layer (summaries prebuilt, one BLAS thread), host CPU"}
 
     src_hash = kernel_source_hash()
     traffic = read_traffic("decode_step_" + args.workload, src_hash)
@@ -509,8 +667,18 @@ def main() -> int:
             "kernel": ("ckv::fused_step_kernel (one launch per decode step)" if launches == 1 else
                        "ckv::step_kernel x3 (score, select, attend; timed together)"),
             "algorithmic_bytes_per_launch": ab["total"], "avg_launch_us": round(avg_launch_us, 3),
-            "launch_timing": f"HIP events around a graph replay of {args.steps} steps on the launch stream, "
-                             f"{launches} launch(es) per step"}
+            "launch_timing": f"HIP events on the launch stream around {replays} back-to-back replays of a "
+                             f"graph of {args.steps // replays} steps, {launches} launch(es) per step"}
+    extra = {}
+    if not args.no_extra and args.workload == "llama_128k":
+        del layers
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        extra["batched_ragged"] = batched_result(args, dev0, n_layers=2)
+        print(f"[bench] batched ragged step in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        t0 = time.time()
+        extra["prefill_128k_loop"] = decode_loop_result(args, dev0, n_layers=args.loop_layers)
+        print(f"[bench] 128K decode loop in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     line = {
         "metric": METRIC, "value": round(us_per_step, 3), "unit": "us/step", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us_per_step / 1e3, 6),
@@ -521,13 +689,15 @@ def main() -> int:
                                f"{w.block_size}, r {w.r_groups}, budget {budget} tokens ({kk} blocks), "
                                f"{args.layers} rotating layer buffers",
                    "global_batch": w.batch, "seq_len": L, "budget_tokens": budget},
+        "distribution_us": distribution(samples),
         "effective_GBps": round(eff_gbps, 1), "pct_hbm_peak": round(100 * eff_gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes": ab, "roofline": roof, "dense": dense,
         "summary_build": {"us": round(build_us, 1),
                           "bytes": kv_all + ab["summary"],
                           "GBps": round((kv_all + ab["summary"]) / (build_us * 1e-6) / 1e9, 1)},
-        "cpu_baseline": cpu, "kernel_source_hash": src_hash,
+        "cpu_baseline": cpu, "workspace_error_word": 0, "kernel_source_hash": src_hash,
     }
+    line.update(extra)
     print(json.dumps(line), flush=True)
     return 0
 

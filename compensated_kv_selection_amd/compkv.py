@@ -34,9 +34,11 @@ EXPORTS = (
     "ckv_decode_step_append_launches",
     "ckv_dense_workspace_bytes",
     "ckv_dense_decode_attention",
+    "ckv_workspace_status",
     "ckv_status_string",
     "ckv_last_error",
 )
+CKV_ERR_INCOMPLETE = 5
 
 
 class CompKVError(RuntimeError):
@@ -84,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ckv_decode_step_append_launches": (I32, [D, I32]),
         "ckv_dense_workspace_bytes": (SZ, [D]),
         "ckv_dense_decode_attention": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
+        "ckv_workspace_status": (I32, [P, SZ, ctypes.POINTER(ctypes.c_uint32), P]),
         "ckv_status_string": (ctypes.c_char_p, [I32]),
         "ckv_last_error": (ctypes.c_char_p, []),
     }
@@ -231,6 +234,15 @@ def workspace_control(ws: torch.Tensor, batch: int, num_kv_heads: int) -> torch.
     pair); the error flag is set if a bounded wait ever ran out."""
     n = CTRL_WORDS_HEADER + CTRL_WORDS_PER_PAIR * batch * num_kv_heads
     return ws[: 4 * n].view(torch.int32).cpu()
+
+
+def workspace_status(workspace: torch.Tensor) -> None:
+    """Wait for the work queued on the current stream, then read and clear the
+    workspace's error word; raise CompKVError (status CKV_ERR_INCOMPLETE) if
+    a call since the last check left it set (its outputs are unspecified)."""
+    word = ctypes.c_uint32(0)
+    _check(load_library().ckv_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                ctypes.byref(word), _stream(workspace.device)))
 
 
 def score_select(dims: Dims, q, summaries: Summaries, block_table, seq_lens, budget_tokens: int,

@@ -9,6 +9,7 @@
 
 #include "../../include/compkv.h"
 #include "internal.hpp"
+#include "plan.hpp"
 
 namespace {
 
@@ -192,53 +193,31 @@ ckv::Summ to_summ(const ckv_summaries* sm) {
   return ckv::Summ{sm->mean_k, sm->mean_v, sm->gvar, sm->count};
 }
 
-// Value workgroups per pair and pairs per round when `pairs` pairs share
-// `cap` resident workgroups: the fewest rounds, then the most value
-// workgroups (one per chunk, down to one per four chunks).  rounds == 0: not
-// even one pair fits.
-struct Fit {
-  int n_val = 0, per_round = 0, rounds = 0;
-};
-Fit fit_pairs(int n_chunks, int cap, int pairs) {
-  Fit best;
-  for (int nv = n_chunks; nv >= (n_chunks + 3) / 4; --nv) {
-    const int per = std::min(pairs, cap / (n_chunks + nv));
-    if (per < 1) continue;
-    const int rounds = (pairs + per - 1) / per;
-    if (best.rounds == 0 || rounds < best.rounds) best = Fit{nv, per, rounds};
-  }
-  return best;
-}
-
-// One launch when its whole grid - at least the control workgroups of every
-// chunk of one (sequence, KV head) pair and a value workgroup per four chunks -
-// can be resident at once, the pair's candidates fit in shared memory and page
-// ids fit in its selection keys; otherwise three launches that never wait.
-// Sets s->bg_round (pairs per round of the persistent grid) and s->n_val when
-// fused.  When blocks go to the device's XCDs round robin (checked once per
-// device, not while `stream` is capturing) and keeping every pair on one XCD
-// takes no more rounds, each pair stays on one XCD (s->n_xcd set), so that its
-// workgroups hand data to each other through that XCD's L2.
+// The single launch's layout on the current device (see plan.hpp).  Whether
+// blocks go to the device's XCDs round robin is checked once per device, and
+// not while `stream` is capturing.  Sets s->bg_round, s->n_val and s->n_xcd.
 bool plan_fused(ckv::Shape* s, hipStream_t stream, bool probe) {
-  if (s->share > ckv::kShareMax || s->n_chunks * s->kmax > ckv::kFusedCand) return false;
-  if (s->P >= (1 << ckv::kFusedPageBits)) return false;
-  const int resident = ckv::fused_resident_workgroups(*s);
-  const int bgs = s->B * s->Hkv;
-  const Fit spread = fit_pairs(s->n_chunks, resident, bgs);
-  if (spread.rounds == 0) return false;
-  s->n_val = spread.n_val;
-  s->bg_round = spread.per_round;
-  s->n_xcd = 0;
+  ckv::plan::Inputs in;
+  in.n_chunks = s->n_chunks;
+  in.kmax = s->kmax;
+  in.share = s->share;
+  in.share_max = ckv::kShareMax;
+  in.cand_max = ckv::kFusedCand;
+  in.num_pages = s->P;
+  in.page_limit = 1 << ckv::kFusedPageBits;
+  in.pairs = s->B * s->Hkv;
+  in.xcds = 0;
+  // the shape rules first, so that a shape that never fuses queries nothing
+  in.resident = 1 << 30;
+  if (!ckv::plan::single_launch(in).single) return false;
+  in.resident = ckv::fused_resident_workgroups(*s);
   const char* off = getenv("CKV_FUSED_ACROSS_XCDS");
-  const int nx = probe && !(off && off[0] == '1') ? ckv::fused_xcd_count(stream) : 0;
-  if (nx > 0) {
-    const Fit local = fit_pairs(s->n_chunks, resident / nx, (bgs + nx - 1) / nx);  // per XCD
-    if (local.rounds > 0 && local.rounds <= spread.rounds) {
-      s->n_xcd = nx;
-      s->n_val = local.n_val;
-      s->bg_round = std::min(bgs, nx * local.per_round);
-    }
-  }
+  in.xcds = probe && !(off && off[0] == '1') ? ckv::fused_xcd_count(stream) : 0;
+  const ckv::plan::Layout L = ckv::plan::single_launch(in);
+  if (!L.single) return false;
+  s->n_val = L.n_val;
+  s->bg_round = L.bg_round;
+  s->n_xcd = L.n_xcd;
   return true;
 }
 
@@ -264,6 +243,7 @@ const char* ckv_status_string(ckv_status st) {
     case CKV_ERR_UNSUPPORTED: return "CKV_ERR_UNSUPPORTED";
     case CKV_ERR_WORKSPACE: return "CKV_ERR_WORKSPACE";
     case CKV_ERR_HIP: return "CKV_ERR_HIP";
+    case CKV_ERR_INCOMPLETE: return "CKV_ERR_INCOMPLETE";
   }
   return "CKV_ERR_UNKNOWN";
 }
@@ -416,6 +396,29 @@ ckv_status ckv_decode_step_append(const ckv_dims* dims, const void* q, const voi
   if (e != hipSuccess) return hip_status(e, "append launch");
   return ckv_decode_step(dims, q, k_cache, v_cache, summaries, block_table, seq_lens, budget_tokens,
                          score_mode, selected, num_selected, out, lse, workspace, workspace_bytes, stream);
+}
+
+ckv_status ckv_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* error_word,
+                                void* stream) {
+  if (error_word) *error_word = 0u;
+  if (!workspace) return fail(CKV_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < 3 * sizeof(uint32_t))
+    return fail(CKV_ERR_INVALID_ARG, "workspace has %zu bytes, the error word needs 12", workspace_bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  CKV_TRY(hip_status(hipStreamIsCapturing(st, &cs), "hipStreamIsCapturing"));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(CKV_ERR_INVALID_ARG, "ckv_workspace_status synchronizes; the stream is capturing a graph");
+  uint32_t* word = static_cast<uint32_t*>(workspace) + 2;
+  uint32_t v = 0u;
+  CKV_TRY(hip_status(hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, st), "error word copy"));
+  CKV_TRY(hip_status(hipStreamSynchronize(st), "hipStreamSynchronize"));
+  if (v == 0u) return ok();
+  if (error_word) *error_word = v;
+  CKV_TRY(hip_status(hipMemsetAsync(word, 0, sizeof v, st), "error word clear"));
+  return fail(CKV_ERR_INCOMPLETE, "error word %u: %s", v,
+              v == 1u ? "a bounded wait between workgroups ran out"
+                      : "a workgroup ran on an XCD it was not placed on");
 }
 
 int32_t ckv_decode_step_append_launches(const ckv_dims* dims, int32_t budget_tokens) {

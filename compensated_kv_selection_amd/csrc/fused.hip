@@ -66,6 +66,7 @@ constexpr int kPollBatch = 8;              // published words read per thread pe
 constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
 constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
 constexpr int kXccProbeBlocks = 256;       // workgroups of the XCD placement check
+constexpr uint32_t kErrPlacement = 2u;     // error word: a workgroup ran on an XCD it was not placed on
 
 template <int D, int G>
 struct CtlLds {
@@ -1160,9 +1161,10 @@ __device__ __forceinline__ void warm_kernel_args() {
 }
 
 template <typename KV, int D, int G, bool kR4, bool kApp>
-__global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, Work w) {
+__global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s_arg, StepIO io, Work w) {
   __shared__ FusedLds<D, G> lds;
   warm_kernel_args();
+  Shape s = s_arg;
   // This workgroup's pair (of the round) and role: control workgroup of
   // chunk `role` (role < n_chunks), else value workgroup role - n_chunks.
   // Kept on one XCD (n_xcd > 0): workgroup i runs on XCD i % n_xcd, which
@@ -1175,6 +1177,16 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s, StepIO io, W
     pair = (int)blockIdx.x % s.n_xcd + s.n_xcd * (slot / wpp);
     role = slot % wpp;
     if (pair >= s.bg_round) return;
+    // The placement rests on workgroup i running on XCD i % n_xcd, checked
+    // once per device before the first launch.  Every workgroup checks it
+    // again: one that runs elsewhere records it in the error word and
+    // writes its published words through to memory.
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+    if (xcc != (uint32_t)((int)blockIdx.x % s.n_xcd)) {
+      if (threadIdx.x == 0) st_c(w.ctrl + 2, kErrPlacement);
+      s.n_xcd = -1;
+    }
   } else {
     const int half = s.bg_round * s.n_chunks;
     if ((int)blockIdx.x < half) {

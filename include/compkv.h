@@ -27,10 +27,16 @@
  * Conventions shared by every call
  * --------------------------------
  * - All array arguments are DEVICE pointers owned by the caller.  The
- *   library allocates no memory and keeps no state between calls, except a
- *   thread-local text describing the last argument error (ckv_last_error).
+ *   library allocates no device memory.  State it keeps between calls: a
+ *   thread-local text describing the last argument error (ckv_last_error);
+ *   per device, the occupancy of each kernel instance (queried once) and
+ *   whether the device sends workgroup i of a launch to XCD i % (number of
+ *   XCDs) (checked once, see ckv_decode_step).
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *   Work is enqueued asynchronously on it; nothing synchronizes the host.
+ *   Work is enqueued asynchronously on it.  Nothing synchronizes the host,
+ *   except ckv_workspace_status and the first ckv_decode_step /
+ *   ckv_decode_step_append (and their *_launches queries) on a device, which
+ *   run the one-time XCD check and wait for it.
  * - Arguments are validated on the host before anything is enqueued.  An
  *   invalid or unsupported argument returns an error status and enqueues
  *   nothing.  A failed kernel launch returns CKV_ERR_HIP.  Faults inside a
@@ -42,7 +48,14 @@
  *   but never an out-of-bounds access.
  * - Inputs must be finite; non-finite inputs give unspecified results.
  * - The library is reentrant; calls on different streams with disjoint
- *   outputs and workspaces may overlap.
+ *   outputs and workspaces may overlap, except that the single launch of
+ *   ckv_decode_step / ckv_decode_step_append (see there) needs the device to
+ *   itself while it runs.
+ * - Kernels whose workgroups wait for each other bound every wait.  A wait
+ *   that runs out, or a workgroup that finds itself on an XCD it was not
+ *   placed on, sets the workspace's error word: the call's outputs are then
+ *   unspecified, although it returned CKV_OK.  ckv_workspace_status reports
+ *   and clears that word; check it where results matter.
  *
  * Layouts (row-major, innermost last)
  * -----------------------------------
@@ -76,7 +89,9 @@ typedef enum {
   CKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent dims */
   CKV_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
   CKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  CKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  CKV_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  CKV_ERR_INCOMPLETE = 5   /* ckv_workspace_status: a call on this workspace did not
+                              complete its work (see there); its outputs are unspecified */
 } ckv_status;
 
 typedef enum { CKV_BF16 = 0, CKV_F32 = 1 } ckv_dtype;
@@ -208,13 +223,50 @@ ckv_status ckv_compensated_decode_attention(const ckv_dims* dims, const void* q,
 
 /* One whole decode step: ckv_score_select followed by
  * ckv_compensated_decode_attention with compensation on, same arguments and
- * results (group scores are not written). */
+ * results (group scores are not written).
+ *
+ * When every chunk of 256 blocks of a (sequence, KV head) pair can be
+ * resident at once (see ckv_decode_step_launches), the step is one
+ * persistent launch whose workgroups hand data to each other through memory
+ * and wait for each other (bounded waits).  The launch is sized to the whole
+ * device, so it must not share the device with other work while it runs:
+ * a kernel running beside it on another stream can keep some of its
+ * workgroups from becoming resident; the waits of the others then run out,
+ * the outputs are unspecified and the workspace's error word is set
+ * (ckv_workspace_status).  Work on the same stream, before or after, is
+ * fine.
+ * The first call on a device (or the first *_launches query) checks, once,
+ * whether the device sends workgroup i of a launch to XCD i % (number of
+ * XCDs): a small kernel on `stream`, waited for with hipStreamSynchronize
+ * (skipped, and the pairs spread over XCDs, if `stream` is capturing a
+ * graph).  If so, all workgroups of a pair run on one XCD and hand data over
+ * in its L2; every workgroup verifies its XCD at entry. */
 ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_cache,
                            const void* v_cache, const ckv_summaries* summaries,
                            const int32_t* block_table, const int32_t* seq_lens,
                            int32_t budget_tokens, int32_t score_mode, int32_t* selected,
                            int32_t* num_selected, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* Reads and clears the error word of a workspace used by ckv_score_select,
+ * ckv_compensated_decode_attention, ckv_decode_step, ckv_decode_step_append
+ * or ckv_dense_decode_attention (uint32 word 2 of the workspace).  Waits for
+ * the work enqueued on `stream` so far, then reads the word.
+ *   CKV_OK: no call on this workspace since the last check (or since it was
+ *     zero-filled) left the word set.
+ *   CKV_ERR_INCOMPLETE: at least one did; the word is cleared (on `stream`)
+ *     and its value stored in *error_word when error_word is not NULL:
+ *     1 = a bounded wait between workgroups ran out (another kernel running
+ *     beside the single launch kept some of its workgroups from becoming
+ *     resident), 2 = a workgroup of the single launch ran on another XCD
+ *     than the one it was placed on.  Outputs of the calls since the last
+ *     check are unspecified.
+ *   CKV_ERR_INVALID_ARG: workspace NULL or smaller than 12 bytes, or `stream`
+ *     is capturing a graph (the call synchronizes).
+ *   CKV_ERR_HIP: the copy or the synchronization failed.
+ * On CKV_OK *error_word (if given) is set to 0. */
+ckv_status ckv_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* error_word,
+                                void* stream);
 
 /* Number of kernel launches ckv_decode_step makes for these dims and budget:
  * 1 when the whole step runs as one persistent launch (every chunk of a

@@ -31,6 +31,7 @@ import torch
 
 from compensated_kv_selection_amd import compkv as C
 from compensated_kv_selection_amd.tensors import to_device, torch_to_storage
+from compensated_kv_selection_amd import workloads as W
 from compensated_kv_selection_amd.workloads import DecodeInputs
 from oracle import compkv_oracle as O
 from ws_layout import PUBLISHED_REGIONS, published_row_words, workspace_regions
@@ -102,6 +103,7 @@ def run_gpu(w: DecodeInputs, budget: Optional[int] = None, score_mode: int = C.S
                                                   dev.block_table, dev.seq_lens, budget, sel, nsel, ws,
                                                   compensate=compensate)
     torch.cuda.synchronize()
+    C.workspace_status(ws)   # raises if a bounded wait ran out or a workgroup left its XCD
     check_workspace_clean(ws, dims, budget)
     return GpuResult(torch_to_storage(summaries.mean_k), torch_to_storage(summaries.mean_v),
                      summaries.gvar.cpu().numpy(), summaries.count.cpu().numpy(),
@@ -186,6 +188,26 @@ def check_selection_isolated(w: DecodeInputs, g: GpuResult, budget: int) -> None
                 assert np.all(g.selected[b, h, kk:kmax] == -1)
 
 
+def check_selection_valid(rank: np.ndarray, kk: int, gsel: np.ndarray, gap: float, osel: np.ndarray,
+                          where: str) -> bool:
+    """Check one (sequence, KV head) selection against the oracle's ranked
+    scores.  A decisive boundary (relative gap >= NEAR_TIE) or an exact tie
+    (gap 0: equal fp64 scores, which the kernels reproduce exactly, e.g.
+    duplicated or constant-key blocks) must give the oracle's set: ties go to
+    the lowest block index.  A near tie (0 < gap < NEAR_TIE) must give a valid
+    top-k within NEAR_TIE: every block clearly above the k-th score taken, no
+    block clearly below it.  Returns True for a near tie."""
+    assert gsel.shape == (kk,) and np.all(np.diff(gsel) > 0), f"{where}: not ascending and distinct"
+    if gap >= NEAR_TIE or gap == 0.0:
+        np.testing.assert_array_equal(gsel, osel, err_msg=where)
+        return False
+    kth = np.sort(rank)[::-1][kk - 1]
+    must = np.nonzero(rank > kth * (1 + NEAR_TIE))[0]
+    assert set(must.tolist()) <= set(gsel.tolist()), f"{where}: missed a clear winner"
+    assert np.all(rank[gsel] >= kth * (1 - NEAR_TIE)), f"{where}: took a clear loser"
+    return True
+
+
 def check_selection_vs_oracle(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]],
                               report: Optional[list] = None) -> int:
     """Returns the number of (seq, KV head) boundaries that were near-ties."""
@@ -196,19 +218,33 @@ def check_selection_vs_oracle(w: DecodeInputs, g: GpuResult, ora: List[Optional[
         kk = o.step.selected.shape[1]
         for h in range(w.num_kv_heads):
             gsel = g.selected[b, h, :kk]
-            osel = o.step.selected[h]
-            if o.step.gaps[h] >= NEAR_TIE:
-                np.testing.assert_array_equal(gsel, osel, err_msg=f"seq {b} KV head {h}")
-            else:
+            if check_selection_valid(o.step.rank_score[h], kk, gsel, float(o.step.gaps[h]),
+                                     o.step.selected[h], f"seq {b} KV head {h}"):
                 near += 1
-                rank = o.step.rank_score[h]
-                kth = np.sort(rank)[::-1][kk - 1]
-                must = np.nonzero(rank > kth * (1 + NEAR_TIE))[0]
-                assert set(must.tolist()) <= set(gsel.tolist()), f"seq {b} head {h}: missed a clear winner"
-                assert np.all(rank[gsel] >= kth * (1 - NEAR_TIE)), f"seq {b} head {h}: took a clear loser"
                 if report is not None:
-                    report.append((b, h, float(o.step.gaps[h]), bool(np.array_equal(gsel, osel))))
+                    report.append((b, h, float(o.step.gaps[h]), bool(np.array_equal(gsel, o.step.selected[h]))))
     return near
+
+
+def check_group_scores(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]], rtol: float = 1e-4) -> int:
+    """The GPU's fp32 ranked scores against the oracle's, element by element,
+    where they are not near fp32's underflow (the kernels form them as
+    exp(log score - log Z_hat), so scores below ~1e-30 of the pair's largest
+    may flush to zero).  Returns the number of scores compared."""
+    n = 0
+    for b, o in enumerate(ora):
+        if o is None:
+            continue
+        M = w.num_blocks(b)
+        for h in range(w.num_kv_heads):
+            ref = o.step.rank_score[h]
+            got = g.group_scores[b, h, :M].astype(np.float64)
+            big = ref > max(1e-30, 1e-25 * ref.max())
+            np.testing.assert_allclose(got[big], ref[big], rtol=rtol, atol=0,
+                                       err_msg=f"group scores seq {b} KV head {h}")
+            assert np.all(got[~big] <= 1e-20), f"seq {b} KV head {h}: tiny scores"
+            n += int(big.sum())
+    return n
 
 
 def oracle_output_for(o: OracleSeq, selected: np.ndarray, w: DecodeInputs, compensate: bool = True):
@@ -234,3 +270,31 @@ def check_outputs(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]],
             lerr = np.abs(g.lse[b][fin] - lse[fin]).max()
             assert lerr <= LSE_ATOL, f"seq {b}: lse error {lerr}"
     return worst
+
+
+def duplicated_blocks_case(seed: int = 77, seq_len: int = 140000, n_copies: int = 12) -> tuple:
+    """A 2-KV-head, 4-query-heads-per-KV-head bf16 workload in which one hot
+    block (keys along the group's mean query, with spread) is copied, keys
+    and values, to n_copies block positions, three of them on both sides of
+    chunk boundaries (blocks 255, 256, 511; chunks are 256 blocks).  Returns
+    (inputs, ascending copy positions).  With a budget of 8 blocks the copies
+    straddle the k-th place, so the selection is decided by the lower-index
+    rule."""
+    w = W.make_decode_inputs(name="dup", seq_lens=[seq_len], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                             r_groups=4, budget_tokens=128, dtype="bf16", n_needles=0, n_outliers=2,
+                             seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    M = w.num_blocks(0)
+    rest = rng.choice(np.arange(512, M - 1), size=n_copies - 3, replace=False)
+    copies = np.unique(np.concatenate([[255, 256, 511], rest]))
+    k, v = w.k_tokens[0], w.v_tokens[0]
+    src = int(copies[-1])
+    q = W.bf16_bits_to_f32(w.q[0])
+    for g in range(2):
+        qm = q[g * 4:(g + 1) * 4].mean(axis=0)
+        hot = 1.0 * qm[None, :] + rng.standard_normal((16, 128), dtype=np.float32)
+        k[src * 16:(src + 1) * 16, g] = W.f32_to_bf16_bits(hot.astype(np.float32))
+    for c in copies[:-1]:
+        k[c * 16:(c + 1) * 16] = k[src * 16:(src + 1) * 16]
+        v[c * 16:(c + 1) * 16] = v[src * 16:(src + 1) * 16]
+    return w, copies

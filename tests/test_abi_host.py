@@ -14,7 +14,7 @@ from ws_layout import workspace_regions
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "compkv.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, INCOMPLETE = range(6)
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
 
 
@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    names = ["CKV_OK", "CKV_ERR_INVALID_ARG", "CKV_ERR_UNSUPPORTED", "CKV_ERR_WORKSPACE", "CKV_ERR_HIP"]
+    names = ["CKV_OK", "CKV_ERR_INVALID_ARG", "CKV_ERR_UNSUPPORTED", "CKV_ERR_WORKSPACE", "CKV_ERR_HIP",
+             "CKV_ERR_INCOMPLETE"]
     for code, name in enumerate(names):
         assert lib.ckv_status_string(code).decode() == name
 
@@ -196,3 +197,13 @@ def test_errors_leave_no_stale_message_after_success_path_text(lib):
     assert lib.ckv_build_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(summ()), None) \
         == UNSUPPORTED
     assert lib.ckv_last_error().decode().startswith("head_dim")
+
+
+def test_workspace_status_rejects_a_missing_or_short_workspace(lib):
+    # checked before any HIP call: the error word is uint32 word 2
+    word = ctypes.c_uint32(7)
+    assert lib.ckv_workspace_status(None, 4096, ctypes.byref(word), None) == INVALID
+    assert "NULL" in lib.ckv_last_error().decode()
+    assert word.value == 0
+    assert lib.ckv_workspace_status(FAKE, 11, ctypes.byref(word), None) == INVALID
+    assert "12" in lib.ckv_last_error().decode()

@@ -9,8 +9,9 @@ from compensated_kv_selection_amd import workloads as W
 from compensated_kv_selection_amd.tensors import dims_of, to_device
 from oracle import compkv_oracle as O
 
-from parity_util import (check_outputs, check_selection_isolated, check_selection_vs_oracle,
-                         check_summaries, check_workspace_clean, run_gpu, run_oracle)
+from parity_util import (check_group_scores, check_outputs, check_selection_isolated,
+                         check_selection_valid, check_selection_vs_oracle, check_summaries,
+                         check_workspace_clean, duplicated_blocks_case, run_gpu, run_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +47,7 @@ def full_check(w, budget=None, score_mode=C.SCORE_COMPKV, compensate=True, fused
         check_summaries(w, g, ora)
         if not fz:
             check_selection_isolated(w, g, budget)
+            check_group_scores(w, g, ora)
         near = check_selection_vs_oracle(w, g, ora, report)
         err = check_outputs(w, g, ora, compensate)
         print(f"[case] ok: max |out - oracle| = {err:.2e}, near-ties {near}", flush=True)
@@ -70,12 +72,18 @@ def test_small_gqa_ragged_bf16(seed):
     full_check(small_gqa(seed))
 
 
-@pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (2, 64, "f32"), (4, 64, "bf16"),
-                                       (8, 128, "bf16"), (8, 64, "f32"), (2, 128, "f32")])
-def test_head_layouts(G, d, dtype):
-    w = W.make_decode_inputs(name=f"G{G}", seq_lens=[2500, 333], num_q_heads=2 * G, num_kv_heads=2,
-                             head_dim=d, r_groups=4, budget_tokens=160, dtype=dtype, n_needles=3,
-                             n_outliers=1, seed=G * 10 + d)
+@pytest.mark.parametrize("r", [4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_every_kernel_instance(dtype, d, G, r):
+    # Every instance the library builds - dtype x head_dim x query heads per
+    # KV head x (r = 4, other r) - through the three-launch path and the
+    # single launch, against the oracle.  Lengths give several chunks of 256
+    # blocks, a ragged tail and a one-chunk sequence.
+    w = W.make_decode_inputs(name=f"inst_{dtype}_d{d}_G{G}_r{r}", seq_lens=[70000, 2500, 333],
+                             num_q_heads=2 * G, num_kv_heads=2, head_dim=d, r_groups=r, budget_tokens=160,
+                             dtype=dtype, n_needles=3, n_outliers=1, seed=G * 10 + d + r)
     full_check(w)
 
 
@@ -112,24 +120,41 @@ def test_fused_step_matches():
     np.testing.assert_allclose(g1.lse, g2.lse, rtol=1e-6, atol=1e-6)
 
 
-def test_constant_key_blocks_give_dense_output():
+@pytest.mark.parametrize("fused", [False, True])
+def test_constant_key_blocks_give_dense_output(fused):
     # Zero within-block variance: every score is 0, ties go to the lowest ids,
-    # and compensation is exact, so the output equals dense attention.
-    w = small_gqa(seed=8, seq_lens=[640, 100])
+    # and compensation is exact, so the output equals dense attention.  The
+    # longer sequence spans two chunks of 256 blocks.
+    w = small_gqa(seed=8, seq_lens=[6000, 100])
     for b in range(w.batch):
         k = w.k_tokens[b]
         L = k.shape[0]
         for i in range(0, L, 16):
             k[i:i + 16] = k[i]
-    g = run_gpu(w, budget=64)
+    g = run_gpu(w, budget=64, fused=fused)
     for b in range(w.batch):
         M = w.num_blocks(b)
-        assert np.all(g.group_scores[b, :, :M] == 0)
+        if not fused:
+            assert np.all(g.group_scores[b, :, :M] == 0)
         np.testing.assert_array_equal(g.selected[b, :, :4], np.tile(np.arange(4), (2, 1)))
         q, k, v = O.sequence_arrays(w.q[b], w.k_tokens[b], w.v_tokens[b], w.dtype)
         out, lse = O.dense_attention(q, k, v)
         assert np.abs(g.out[b] - out).max() <= 2e-3
         assert np.abs(g.lse[b] - lse).max() <= 1e-4
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_duplicated_blocks_tie_to_the_lowest_index(fused):
+    # Twelve copies of one hot block, three across chunk boundaries, a budget
+    # of 8 blocks: the copies' scores are equal and straddle the k-th place,
+    # so the lower block ids win, on both paths.
+    w, copies = duplicated_blocks_case()
+    g, ora = full_check(w, fused=fused)
+    for h in range(2):
+        rank = ora[0].step.rank_score[h]
+        assert np.all(rank[copies] == rank[copies[0]])
+        assert ora[0].step.gaps[h] == 0.0
+        np.testing.assert_array_equal(g.selected[0, h, :8], copies[:8])
 
 
 def _dense_check(w):
@@ -380,9 +405,10 @@ def test_prefill_then_decode_loop(fused_append):
             g_sel = sel.cpu().numpy()[0]
             kk = res.selected.shape[1]
             assert np.all(nsel.cpu().numpy()[0] == kk)
+            C.workspace_status(ws)
             for h in range(8):
-                if res.gaps[h] >= 1e-5:
-                    np.testing.assert_array_equal(g_sel[h, :kk], res.selected[h])
+                check_selection_valid(res.rank_score[h], kk, g_sel[h, :kk], float(res.gaps[h]),
+                                      res.selected[h], f"step {t} KV head {h}")
             o2, l2 = O.compensated_attention(q, k64[:L + 1], v64[:L + 1], osumm,
                                              g_sel[:, :kk].astype(np.int64), 16)
             assert np.abs(out.cpu().numpy()[0] - o2).max() <= 2e-3
@@ -428,6 +454,32 @@ def test_decode_loop_graph_replays_match_eager():
         for name, x, r in zip(("out", "lse", "num_selected", "selected"), outs, ref):
             assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager loop"
         check_workspace_clean(loop.ws, dims, w.budget_tokens)
+
+
+def _oracle_check_paged(w, q_dev, k_cache, v_cache, lens, budget, result):
+    """Check a decode step's (selected, num_selected, out, lse) against the
+    oracle run on the given device caches, read back token by token through
+    the page table for the given lengths."""
+    from compensated_kv_selection_amd.tensors import torch_to_storage
+    sel, nsel, out, lse = (x.cpu().numpy() for x in result)
+    kc, vc = torch_to_storage(k_cache), torch_to_storage(v_cache)
+    qs = torch_to_storage(q_dev)
+    for b, L in enumerate(lens.tolist()):
+        if L == 0:
+            continue
+        pages = w.block_table[b, np.arange(L) // 16]
+        slots = np.arange(L) % 16
+        q, k, v = O.sequence_arrays(qs[b], kc[pages, :, slots, :], vc[pages, :, slots, :], w.dtype)
+        summ = O.build_summaries(k, v, 16, w.r_groups, w.dtype)
+        res = O.decode_step(q, k, v, summ, budget_tokens=budget, block_size=16, r=w.r_groups)
+        kk = res.selected.shape[1]
+        assert np.all(nsel[b] == kk)
+        for g in range(w.num_kv_heads):
+            check_selection_valid(res.rank_score[g], kk, sel[b, g, :kk], float(res.gaps[g]), res.selected[g],
+                                  f"seq {b} KV head {g}")
+        o2, l2 = O.compensated_attention(q, k, v, summ, sel[b, :, :kk].astype(np.int64), 16)
+        assert np.abs(out[b] - o2).max() <= 2e-3, (b, float(np.abs(out[b] - o2).max()))
+        assert np.abs(lse[b] - l2).max() <= 1e-4
 
 
 def _append_step_case(before, num_kv_heads, budget, seed, hot, steps=3, G=4, d=128, r=4, dtype="bf16"):
@@ -517,6 +569,9 @@ def test_decode_step_append_matches_append_then_step(before, num_kv_heads, budge
                               (sb.mean_k, sb.mean_v, sb.gvar, sb.count)):
             assert torch.equal(bits(x), bits(y)), f"step {step}: summary {name} differs"
         check_workspace_clean(wsb, dims, budget)
+    # the appending step's last results against the oracle, on the caches
+    # it wrote (read back from the device through the page table)
+    _oracle_check_paged(w, dev.q, kb, vb, lens, budget, rb)
     # the hot sequences did attend to their tail block
     for b in hot:
         L = int(lens[b])
