@@ -93,7 +93,7 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
 }
 
 struct Layout {
-  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, fw, fpart, total;
+  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, fw, fpart, fsmp, total;
 };
 
 size_t ctrl_bytes(const ckv::Shape& s) {
@@ -103,7 +103,7 @@ size_t ctrl_bytes(const ckv::Shape& s) {
 // Sparse-step workspace: control words, per-block scores, chunk partials,
 // first-level select candidates, gather partials, and what the fused step
 // hands between workgroups: chunk headers and candidates (zero between
-// calls), tagged compensation weights, and chunk partials.
+// calls), tagged compensation weights, chunk partials and chunk samples.
 Layout layout(const ckv::Shape& s) {
   Layout L;
   const size_t pst = ckv::kPartStride(s.D);
@@ -128,6 +128,8 @@ Layout layout(const ckv::Shape& s) {
   off += align_up(bg * s.n_chunks * s.G * (ckv::kChunk + 1) * sizeof(uint64_t));
   L.fpart = off;
   off += align_up(bg * 2 * s.n_chunks * s.G * (size_t)(s.D + 2) * sizeof(uint64_t));
+  L.fsmp = off;
+  off += align_up(bg * s.n_chunks * 4 * s.G * sizeof(uint64_t));
   L.total = off;
   return L;
 }
@@ -139,7 +141,7 @@ ckv::Work carve(const ckv::Shape& s, void* ws) {
                    reinterpret_cast<float*>(base + L.cpart), reinterpret_cast<uint64_t*>(base + L.cand),
                    reinterpret_cast<float*>(base + L.gpart), reinterpret_cast<uint64_t*>(base + L.fhdr),
                    reinterpret_cast<uint64_t*>(base + L.fcand), reinterpret_cast<uint64_t*>(base + L.fw),
-                   reinterpret_cast<uint64_t*>(base + L.fpart)};
+                   reinterpret_cast<uint64_t*>(base + L.fpart), reinterpret_cast<uint64_t*>(base + L.fsmp)};
 }
 
 // Dense splits: about 256 workgroups in all (one per CU), a
@@ -230,6 +232,38 @@ bool plan_fused_append(ckv::Shape* s, hipStream_t stream, bool probe) {
   if (plan_fused(s, stream, probe) && s->n_xcd > 0) return true;
   s->append = 0;
   return false;
+}
+
+// The arguments of ckv_decode_step other than the workspace.
+ckv_status check_step_args(const ckv_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                           const ckv_summaries* summaries, const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t budget_tokens, int32_t score_mode, const int32_t* selected,
+                           const int32_t* num_selected, const float* out, ckv::Shape* s) {
+  if (budget_tokens < 0) return fail(CKV_ERR_INVALID_ARG, "budget_tokens must be >= 0");
+  CKV_TRY(make_shape(dims, budget_tokens, s));
+  if (!q || !k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "q, k_cache or v_cache is NULL");
+  if (!block_table || !seq_lens) return fail(CKV_ERR_INVALID_ARG, "block_table or seq_lens is NULL");
+  if (!num_selected || (!selected && s->kmax > 0))
+    return fail(CKV_ERR_INVALID_ARG, "selected or num_selected is NULL");
+  if (!out) return fail(CKV_ERR_INVALID_ARG, "out is NULL");
+  if (score_mode != CKV_SCORE_COMPKV && score_mode != CKV_SCORE_MASS)
+    return fail(CKV_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+  return check_summaries(summaries);
+}
+
+// One decode step on checked arguments and a workspace of the step's layout.
+ckv_status decode_step_launches(ckv::Shape s, const void* q, const void* k_cache, const void* v_cache,
+                                const ckv_summaries* summaries, const int32_t* block_table,
+                                const int32_t* seq_lens, int32_t score_mode, int32_t* selected,
+                                int32_t* num_selected, float* out, float* lse, void* workspace, hipStream_t st) {
+  ckv::StepIO io{q, k_cache, v_cache, to_summ(summaries), block_table, seq_lens, selected,
+                 num_selected, nullptr, out, lse, score_mode, 1};
+  const ckv::Work w = carve(s, workspace);
+  if (plan_fused(&s, st, true)) return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
+  hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
+  if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
+  if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
+  return hip_status(e, "decode step launches");
 }
 
 }  // namespace
@@ -342,27 +376,12 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
                            int32_t budget_tokens, int32_t score_mode, int32_t* selected,
                            int32_t* num_selected, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  if (budget_tokens < 0) return fail(CKV_ERR_INVALID_ARG, "budget_tokens must be >= 0");
   ckv::Shape s;
-  CKV_TRY(make_shape(dims, budget_tokens, &s));
-  if (!q || !k_cache || !v_cache) return fail(CKV_ERR_INVALID_ARG, "q, k_cache or v_cache is NULL");
-  if (!block_table || !seq_lens) return fail(CKV_ERR_INVALID_ARG, "block_table or seq_lens is NULL");
-  if (!num_selected || (!selected && s.kmax > 0))
-    return fail(CKV_ERR_INVALID_ARG, "selected or num_selected is NULL");
-  if (!out) return fail(CKV_ERR_INVALID_ARG, "out is NULL");
-  if (score_mode != CKV_SCORE_COMPKV && score_mode != CKV_SCORE_MASS)
-    return fail(CKV_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
-  CKV_TRY(check_summaries(summaries));
+  CKV_TRY(check_step_args(dims, q, k_cache, v_cache, summaries, block_table, seq_lens, budget_tokens,
+                          score_mode, selected, num_selected, out, &s));
   CKV_TRY(check_workspace(s, workspace, workspace_bytes));
-  ckv::StepIO io{q, k_cache, v_cache, to_summ(summaries), block_table, seq_lens, selected,
-                 num_selected, nullptr, out, lse, score_mode, 1};
-  const ckv::Work w = carve(s, workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (plan_fused(&s, st, true)) return hip_status(ckv::launch_fused(s, io, w, st), "decode step launch");
-  hipError_t e = ckv::launch_step(s, ckv::kModeScanOnly, io, w, st);
-  if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeSelectOnly, io, w, st);
-  if (e == hipSuccess) e = ckv::launch_step(s, ckv::kModeAttendOnly, io, w, st);
-  return hip_status(e, "decode step launches");
+  return decode_step_launches(s, q, k_cache, v_cache, summaries, block_table, seq_lens, score_mode, selected,
+                              num_selected, out, lse, workspace, static_cast<hipStream_t>(stream));
 }
 
 ckv_status ckv_decode_step_append(const ckv_dims* dims, const void* q, const void* k_new,
@@ -459,7 +478,7 @@ ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const
     return fail(CKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(workspace);
   ckv::Work w{reinterpret_cast<uint32_t*>(base), nullptr, nullptr, nullptr,
-              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr, nullptr, nullptr};
+              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr, nullptr, nullptr, nullptr};
   ckv::StepIO io{q, k_cache, v_cache, ckv::Summ{nullptr, nullptr, nullptr, nullptr}, block_table,
                  seq_lens, nullptr, nullptr, nullptr, out, lse, 0, 0};
   return hip_status(ckv::launch_step(s, ckv::kModeDense, io, w, static_cast<hipStream_t>(stream)),

@@ -74,6 +74,8 @@ struct Work {
                    //   max, tagged
   uint64_t* fpart; // [B][Hkv][2 * n_chunks][G][D+2] fused: control and value partials
                    //   (max, sum, acc[D]), tagged
+  uint64_t* fsmp;  // [B][Hkv][n_chunks][4][G] fused: per chunk, four sample blocks' per-head
+                   //   log-scores, tagged
 };
 
 struct Summ {
@@ -128,7 +130,8 @@ int fused_resident_workgroups(const Shape& s);
 hipError_t launch_fused(const Shape& s, const StepIO& io, const Work& w, hipStream_t stream);
 
 // Number of XCDs if the device sends workgroup i of a launch to XCD
-// i % (number of XCDs), else 0.  Checked once per device with a small kernel
+// (i + c) % (number of XCDs), c the same for every workgroup of the launch,
+// else 0.  Checked once per device with a small kernel
 // on `stream` (waits for it); returns 0 without checking while `stream` is
 // capturing a graph.
 int fused_xcd_count(hipStream_t stream);

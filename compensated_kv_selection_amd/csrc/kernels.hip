@@ -586,23 +586,6 @@ struct DenseCfg {
   static constexpr int NR = CPL / 8;            // eight-element loads per row
 };
 
-__device__ __forceinline__ uint32_t dpp_row_half_mirror(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t dpp_row_mirror(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
-}
-// Sum over each group of LPT consecutive lanes (LPT = 4, 8, 16); every lane
-// of a group receives the same value.
-template <int LPT>
-__device__ __forceinline__ float token_row_sum(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = OpFadd{}(u, dpp_quad_xor1(u));
-  u = OpFadd{}(u, dpp_quad_xor2(u));
-  if (LPT >= 8) u = OpFadd{}(u, dpp_row_half_mirror(u));
-  if (LPT >= 16) u = OpFadd{}(u, dpp_row_mirror(u));
-  return __uint_as_float(u);
-}
 // Reduction over the lanes that hold the same channels (lane % LPT) in the
 // wave's 64 / LPT token slots.
 template <int LPT, class Op>

@@ -13,6 +13,7 @@ namespace ckv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -205,6 +206,12 @@ __device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t x) {
 __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);
 }
+__device__ __forceinline__ uint32_t dpp_row_half_mirror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_mirror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);
+}
 // Combine 16-lane rows pairwise (rows 0-1, 2-3), then wave halves; each
 // result lane sees (low operand, high operand) in the same order.
 template <class Op>
@@ -236,6 +243,17 @@ struct OpFadd {
     return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
   }
 };
+// Sum over each group of LPT consecutive lanes (LPT = 4, 8, 16) by DPP
+// swaps within a row; every lane of a group receives the same value.
+template <int LPT>
+__device__ __forceinline__ float token_row_sum(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = OpFadd{}(u, dpp_quad_xor1(u));
+  u = OpFadd{}(u, dpp_quad_xor2(u));
+  if (LPT >= 8) u = OpFadd{}(u, dpp_row_half_mirror(u));
+  if (LPT >= 16) u = OpFadd{}(u, dpp_row_mirror(u));
+  return __uint_as_float(u);
+}
 __device__ __forceinline__ float wave_max_dpp(float x) { return __uint_as_float(wave_reduce(__float_as_uint(x), OpFmax{})); }
 __device__ __forceinline__ float wave_sum_dpp(float x) { return __uint_as_float(wave_reduce(__float_as_uint(x), OpFadd{})); }
 

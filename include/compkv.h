@@ -236,11 +236,12 @@ ckv_status ckv_compensated_decode_attention(const ckv_dims* dims, const void* q,
  * (ckv_workspace_status).  Work on the same stream, before or after, is
  * fine.
  * The first call on a device (or the first *_launches query) checks, once,
- * whether the device sends workgroup i of a launch to XCD i % (number of
- * XCDs): a small kernel on `stream`, waited for with hipStreamSynchronize
- * (skipped, and the pairs spread over XCDs, if `stream` is capturing a
- * graph).  If so, all workgroups of a pair run on one XCD and hand data over
- * in its L2; every workgroup verifies its XCD at entry. */
+ * whether the device sends the workgroups of a launch to its XCDs in turn
+ * (workgroup i to XCD (i + c) % (number of XCDs), c fixed within a launch):
+ * a small kernel on `stream`, waited for with hipStreamSynchronize (skipped,
+ * and the pairs spread over XCDs, if `stream` is capturing a graph).  If so,
+ * every workgroup reads the XCD it runs on and takes a role of a pair placed
+ * on that XCD, so that a pair's workgroups hand data over in one L2. */
 ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_cache,
                            const void* v_cache, const ckv_summaries* summaries,
                            const int32_t* block_table, const int32_t* seq_lens,
@@ -258,8 +259,9 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
  *     and its value stored in *error_word when error_word is not NULL:
  *     1 = a bounded wait between workgroups ran out (another kernel running
  *     beside the single launch kept some of its workgroups from becoming
- *     resident), 2 = a workgroup of the single launch ran on another XCD
- *     than the one it was placed on.  Outputs of the calls since the last
+ *     resident, or the device stopped sending workgroups to its XCDs in
+ *     turn), 2 = a workgroup of the single launch ran on an XCD that the
+ *     one-time check did not see.  Outputs of the calls since the last
  *     check are unspecified.
  *   CKV_ERR_INVALID_ARG: workspace NULL or smaller than 12 bytes, or `stream`
  *     is capturing a graph (the call synchronizes).

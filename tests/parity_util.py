@@ -59,7 +59,8 @@ def check_workspace_clean(ws, dims, budget):
     the fused step's published headers and candidates zero, ready for the
     next call."""
     ctrl = C.workspace_control(ws, dims.batch, dims.num_kv_heads)
-    assert int(ctrl[2]) == 0, "a bounded wait in the step kernel ran out"
+    assert int(ctrl[2]) == 0, (f"error word {int(ctrl[2])} (1: a bounded wait ran out, 2: a workgroup ran on "
+                               f"an XCD it was not placed on); header words {ctrl[:8].tolist()}")
     ctrl = ctrl.clone()
     ctrl[C.CTRL_WORDS_HEADER + C.CTRL_EPOCH::C.CTRL_WORDS_PER_PAIR] = 0
     assert int(ctrl.abs().sum()) == 0, f"control words not reset: {ctrl.nonzero().flatten().tolist()}"
@@ -227,8 +228,12 @@ def check_selection_vs_oracle(w: DecodeInputs, g: GpuResult, ora: List[Optional[
 
 
 def check_group_scores(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleSeq]], rtol: float = 1e-4) -> int:
-    """The GPU's fp32 ranked scores against the oracle's, element by element,
-    where they are not near fp32's underflow (the kernels form them as
+    """The GPU's fp32 ranked scores against the oracle's, element by element.
+    Compared where the block's stored mean key is the same on both sides
+    (bf16: the two roundings of the mean can land one unit apart, which
+    moves that block's logit by up to tau |q| 2^-8 |mean|, far more than the
+    scoring arithmetic's error; such blocks are counted and must be rare)
+    and where the score is not near fp32's underflow (the kernels form
     exp(log score - log Z_hat), so scores below ~1e-30 of the pair's largest
     may flush to zero).  Returns the number of scores compared."""
     n = 0
@@ -236,14 +241,21 @@ def check_group_scores(w: DecodeInputs, g: GpuResult, ora: List[Optional[OracleS
         if o is None:
             continue
         M = w.num_blocks(b)
+        if w.dtype == "bf16":
+            gk = (g.mean_k[b, :, :M].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        else:
+            gk = g.mean_k[b, :, :M].astype(np.float64)
+        same_row = np.all(gk == o.summ.mean_k.transpose(1, 0, 2), axis=2)   # [Hkv, M]
         for h in range(w.num_kv_heads):
             ref = o.step.rank_score[h]
             got = g.group_scores[b, h, :M].astype(np.float64)
             big = ref > max(1e-30, 1e-25 * ref.max())
-            np.testing.assert_allclose(got[big], ref[big], rtol=rtol, atol=0,
+            cmp = big & same_row[h] if w.dtype == "bf16" else big
+            assert cmp.sum() >= 0.99 * big.sum(), f"seq {b} KV head {h}: too many differing mean keys"
+            np.testing.assert_allclose(got[cmp], ref[cmp], rtol=rtol, atol=0,
                                        err_msg=f"group scores seq {b} KV head {h}")
             assert np.all(got[~big] <= 1e-20), f"seq {b} KV head {h}: tiny scores"
-            n += int(big.sum())
+            n += int(cmp.sum())
     return n
 
 
