@@ -35,10 +35,12 @@ EXPORTS = (
     "ckv_dense_workspace_bytes",
     "ckv_dense_decode_attention",
     "ckv_workspace_status",
+    "ckv_decode_step_noalloc",
     "ckv_status_string",
     "ckv_last_error",
 )
 CKV_ERR_INCOMPLETE = 5
+CKV_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class CompKVError(RuntimeError):
@@ -87,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ckv_dense_workspace_bytes": (SZ, [D]),
         "ckv_dense_decode_attention": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "ckv_workspace_status": (I32, [P, SZ, ctypes.POINTER(ctypes.c_uint32), P]),
+        "ckv_decode_step_noalloc": (I32, [D, P, P, P, S, P, P, I32, I32, P, P, P, P, P]),
         "ckv_status_string": (ctypes.c_char_p, [I32]),
         "ckv_last_error": (ctypes.c_char_p, []),
     }
@@ -245,6 +248,14 @@ def workspace_status(workspace: torch.Tensor) -> None:
                                                 ctypes.byref(word), _stream(workspace.device)))
 
 
+def noalloc_status(device) -> None:
+    """workspace_status for the built-in workspace of decode_step_noalloc on
+    `device` (made current for the call)."""
+    word = ctypes.c_uint32(0)
+    with torch.cuda.device(device):
+        _check(load_library().ckv_workspace_status(None, 0, ctypes.byref(word), _stream(torch.device(device))))
+
+
 def score_select(dims: Dims, q, summaries: Summaries, block_table, seq_lens, budget_tokens: int,
                  workspace: torch.Tensor, score_mode: int = SCORE_COMPKV, selected=None,
                  num_selected=None, group_scores=None):
@@ -305,6 +316,33 @@ def decode_step(dims: Dims, q, k_cache, v_cache, summaries: Summaries, block_tab
         ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(s), _ptr(block_table),
         _ptr(seq_lens), budget_tokens, score_mode, _ptr(selected), _ptr(num_selected), _ptr(out),
         _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return selected, num_selected, out, lse
+
+
+def decode_step_noalloc(dims: Dims, q, k_cache, v_cache, summaries: Summaries, block_table, seq_lens,
+                        budget_tokens: int, score_mode: int = SCORE_COMPKV, selected=None, num_selected=None,
+                        out=None, lse=None):
+    """decode_step in the library's built-in workspace (the library
+    allocates nothing; outputs not passed in are allocated here by torch)."""
+    lib = load_library()
+    dev = q.device
+    B, H = dims.batch, dims.num_kv_heads
+    kmax = dims.kmax(budget_tokens)
+    if selected is None:
+        selected = torch.empty((B, H, max(kmax, 1)), dtype=torch.int32, device=dev)
+    if num_selected is None:
+        num_selected = torch.empty((B, H), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=dev)
+    d = dims.c()
+    s = summaries.c()
+    with torch.cuda.device(dev):
+        _check(lib.ckv_decode_step_noalloc(
+            ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(s), _ptr(block_table),
+            _ptr(seq_lens), budget_tokens, score_mode, _ptr(selected), _ptr(num_selected), _ptr(out),
+            _ptr(lse), _stream(dev)))
     return selected, num_selected, out, lse
 
 

@@ -2,6 +2,7 @@
 // launch order.  Every check runs before anything is enqueued.
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -10,6 +11,12 @@
 #include "../../include/compkv.h"
 #include "internal.hpp"
 #include "plan.hpp"
+
+// The workspace of ckv_decode_step_noalloc: one copy per device, held until
+// the process ends.  Host code never passes this name to a kernel or a copy
+// (on the host it is only a stand-in for the symbol): it uses the device
+// address that hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) unsigned char scratch[CKV_NOALLOC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -266,6 +273,48 @@ ckv_status decode_step_launches(ckv::Shape s, const void* q, const void* k_cache
   return hip_status(e, "decode step launches");
 }
 
+// ---- the built-in workspace of ckv_decode_step_noalloc ----
+constexpr int kScratchDevices = 64;
+struct ScratchState {
+  void* ptr = nullptr;    // this device's copy of `scratch`
+  bool laid_out = false;  // holds the clean state of the last call's layout:
+  ckv_dims dims{};        //   these dims
+  int32_t budget = -1;    //   and this budget
+};
+std::mutex g_scratch_mu;
+ScratchState g_scratch[kScratchDevices];
+
+bool same_dims(const ckv_dims& a, const ckv_dims& b) {
+  return a.batch == b.batch && a.num_q_heads == b.num_q_heads && a.num_kv_heads == b.num_kv_heads &&
+         a.head_dim == b.head_dim && a.block_size == b.block_size && a.r_groups == b.r_groups &&
+         a.num_pages == b.num_pages && a.max_blocks_per_seq == b.max_blocks_per_seq && a.kv_dtype == b.kv_dtype;
+}
+
+__global__ void zero_fill_kernel(uint4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's state, its scratch address looked up on first use
+// (with the device current).  Called with g_scratch_mu held.
+ckv_status scratch_state(ScratchState** out) {
+  int dev = 0;
+  CKV_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(CKV_ERR_UNSUPPORTED, "device %d: the built-in workspace serves devices 0..%d", dev,
+                kScratchDevices - 1);
+  ScratchState& z = g_scratch[dev];
+  if (!z.ptr) {
+    void* p = nullptr;
+    CKV_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256)
+      return fail(CKV_ERR_HIP, "hipGetSymbolAddress(scratch) gave an unusable address %p", p);
+    z.ptr = p;
+  }
+  *out = &z;
+  return CKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,6 +469,15 @@ ckv_status ckv_decode_step_append(const ckv_dims* dims, const void* q, const voi
 ckv_status ckv_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* error_word,
                                 void* stream) {
   if (error_word) *error_word = 0u;
+  if (!workspace && workspace_bytes == 0) {
+    // the built-in workspace of ckv_decode_step_noalloc on the current device
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchState* z = nullptr;
+    CKV_TRY(scratch_state(&z));
+    const ckv_status st = ckv_workspace_status(z->ptr, CKV_NOALLOC_WORKSPACE_BYTES, error_word, stream);
+    if (st == CKV_ERR_INCOMPLETE) z->laid_out = false;  // the next call starts from a cleared workspace
+    return st;
+  }
   if (!workspace) return fail(CKV_ERR_INVALID_ARG, "workspace is NULL");
   if (workspace_bytes < 3 * sizeof(uint32_t))
     return fail(CKV_ERR_INVALID_ARG, "workspace has %zu bytes, the error word needs 12", workspace_bytes);
@@ -438,6 +496,37 @@ ckv_status ckv_workspace_status(void* workspace, size_t workspace_bytes, uint32_
   return fail(CKV_ERR_INCOMPLETE, "error word %u: %s", v,
               v == 1u ? "a bounded wait between workgroups ran out"
                       : "a workgroup ran on an XCD it was not placed on");
+}
+
+ckv_status ckv_decode_step_noalloc(const ckv_dims* dims, const void* q, const void* k_cache,
+                                   const void* v_cache, const ckv_summaries* summaries,
+                                   const int32_t* block_table, const int32_t* seq_lens, int32_t budget_tokens,
+                                   int32_t score_mode, int32_t* selected, int32_t* num_selected, float* out,
+                                   float* lse, void* stream) {
+  ckv::Shape s;
+  CKV_TRY(check_step_args(dims, q, k_cache, v_cache, summaries, block_table, seq_lens, budget_tokens,
+                          score_mode, selected, num_selected, out, &s));
+  const size_t need = layout(s).total;
+  if (need > CKV_NOALLOC_WORKSPACE_BYTES)
+    return fail(CKV_ERR_WORKSPACE, "the step needs %zu bytes of workspace; the built-in one holds %zu", need,
+                (size_t)CKV_NOALLOC_WORKSPACE_BYTES);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState* z = nullptr;
+  CKV_TRY(scratch_state(&z));
+  if (!z->laid_out || z->budget != budget_tokens || !same_dims(z->dims, *dims)) {
+    // a new layout: its control and hand-off words start at zero, as in a
+    // freshly cleared workspace
+    const size_t n = need / sizeof(uint4);  // need is a multiple of 256
+    const unsigned grid = (unsigned)std::min<size_t>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, st, static_cast<uint4*>(z->ptr), n);
+    CKV_TRY(hip_status(hipGetLastError(), "workspace clear launch"));
+    z->dims = *dims;
+    z->budget = budget_tokens;
+    z->laid_out = true;
+  }
+  return decode_step_launches(s, q, k_cache, v_cache, summaries, block_table, seq_lens, score_mode, selected,
+                              num_selected, out, lse, z->ptr, st);
 }
 
 int32_t ckv_decode_step_append_launches(const ckv_dims* dims, int32_t budget_tokens) {

@@ -263,12 +263,47 @@ ckv_status ckv_decode_step(const ckv_dims* dims, const void* q, const void* k_ca
  *     turn), 2 = a workgroup of the single launch ran on an XCD that the
  *     one-time check did not see.  Outputs of the calls since the last
  *     check are unspecified.
- *   CKV_ERR_INVALID_ARG: workspace NULL or smaller than 12 bytes, or `stream`
- *     is capturing a graph (the call synchronizes).
+ *   CKV_ERR_INVALID_ARG: workspace NULL (with workspace_bytes > 0) or
+ *     smaller than 12 bytes, or `stream` is capturing a graph (the call
+ *     synchronizes).
  *   CKV_ERR_HIP: the copy or the synchronization failed.
+ * workspace NULL with workspace_bytes 0 names the built-in workspace of
+ * ckv_decode_step_noalloc on the current device (CKV_OK if no call has used
+ * it); after it reports CKV_ERR_INCOMPLETE, the next ckv_decode_step_noalloc
+ * call on the device clears that workspace before it starts.
  * On CKV_OK *error_word (if given) is set to 0. */
 ckv_status ckv_workspace_status(void* workspace, size_t workspace_bytes, uint32_t* error_word,
                                 void* stream);
+
+/* Size of the workspace built into the library for ckv_decode_step_noalloc:
+ * one per device the library runs on, held until the process ends. */
+#define CKV_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* ckv_decode_step for callers that cannot allocate device memory: code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as ckv_decode_step, except that there
+ * is no workspace argument: the step runs in a workspace built into the
+ * library, CKV_NOALLOC_WORKSPACE_BYTES on each device, which covers, for
+ * example, 16 sequences of 64K tokens with 8 KV heads, d = 128 and a budget
+ * of 1024 tokens (55 MiB).  The call allocates nothing.
+ *   CKV_ERR_WORKSPACE: ckv_workspace_bytes(dims, budget_tokens) is larger
+ *     than CKV_NOALLOC_WORKSPACE_BYTES (checked before anything is enqueued).
+ *   CKV_ERR_UNSUPPORTED: the current device's ordinal is 64 or more.
+ * Every call on a device shares that device's built-in workspace, which
+ * keeps the state the last call left: calls on one stream are ordered, but
+ * calls that overlap on one device (other streams, other threads) race, and
+ * their outputs are unspecified.  The first call on a device, and every call
+ * whose dims or budget differ from the previous call's there, first clears
+ * the bytes the step uses with a fill kernel on `stream` (inside a captured
+ * graph that clear is captured too; an eager call with the same dims and
+ * budget before the capture keeps it out).  The first call on a device looks
+ * up the built-in workspace's address on it.  ckv_workspace_status(NULL, 0,
+ * ...) reads its error word. */
+ckv_status ckv_decode_step_noalloc(const ckv_dims* dims, const void* q, const void* k_cache,
+                                   const void* v_cache, const ckv_summaries* summaries,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int32_t budget_tokens, int32_t score_mode, int32_t* selected,
+                                   int32_t* num_selected, float* out, float* lse, void* stream);
 
 /* Number of kernel launches ckv_decode_step makes for these dims and budget:
  * 1 when the whole step runs as one persistent launch (every chunk of a

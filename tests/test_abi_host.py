@@ -96,6 +96,8 @@ def test_bad_dims_rejected_everywhere(lib, kw, status, needle):
                                     FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None),
         lambda: lib.ckv_dense_decode_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                                FAKE, 1 << 40, None),
+        lambda: lib.ckv_decode_step_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, FAKE, 512,
+                                            0, FAKE, FAKE, FAKE, None, None),
     ]
     for call in calls:
         assert call() == status
@@ -207,3 +209,37 @@ def test_workspace_status_rejects_a_missing_or_short_workspace(lib):
     assert word.value == 0
     assert lib.ckv_workspace_status(FAKE, 11, ctypes.byref(word), None) == INVALID
     assert "12" in lib.ckv_last_error().decode()
+
+
+def test_noalloc_step_checks_its_arguments_first(lib):
+    # every argument check of ckv_decode_step, before any HIP call
+    d = good_dims()
+    s = summ()
+    args = [FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, FAKE, 512, 0, FAKE, FAKE, FAKE, None, None]
+    for i in (0, 1, 2, 3, 4, 5, 8, 9, 10):  # q, k, v, summaries, block_table, seq_lens, selected, num, out
+        a = list(args)
+        a[i] = None
+        assert lib.ckv_decode_step_noalloc(ctypes.byref(d), *a) == INVALID
+    a = list(args)
+    a[6] = -1
+    assert lib.ckv_decode_step_noalloc(ctypes.byref(d), *a) == INVALID
+    assert "budget" in lib.ckv_last_error().decode()
+    a = list(args)
+    a[7] = 9
+    assert lib.ckv_decode_step_noalloc(ctypes.byref(d), *a) == INVALID
+    assert "score_mode" in lib.ckv_last_error().decode()
+
+
+def test_noalloc_step_rejects_a_layout_beyond_its_workspace(lib):
+    s = summ()
+    limit = C.CKV_NOALLOC_WORKSPACE_BYTES
+    # 16 sequences of 64K tokens with a 1024-token budget fit; 32 of 128K do not
+    fits = good_dims(batch=16, max_blocks_per_seq=4096, num_pages=16 * 4096)
+    assert 0 < lib.ckv_workspace_bytes(ctypes.byref(fits), 1024) <= limit
+    big = good_dims(batch=32, max_blocks_per_seq=8192, num_pages=32 * 8192)
+    need = lib.ckv_workspace_bytes(ctypes.byref(big), 512)
+    assert need > limit
+    assert lib.ckv_decode_step_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, FAKE, 512, 0,
+                                       FAKE, FAKE, FAKE, None, None) == WORKSPACE
+    msg = lib.ckv_last_error().decode()
+    assert str(need) in msg and str(limit) in msg
