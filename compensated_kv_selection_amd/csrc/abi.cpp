@@ -87,6 +87,8 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
   x.n_xcd = 0;
   x.n_val = x.n_chunks;
   int splits = (x.kmax + ckv::kGatherPages - 1) / ckv::kGatherPages;
+  splits = std::min(splits, std::max(1, ckv::kGatherGroups / (x.B * x.Hkv)));
+  splits = std::max(splits, (x.kmax + ckv::kShareMax - 1) / ckv::kShareMax);  // a split's blocks fit its LDS
   splits = splits < 1 ? 1 : (splits > ckv::kMaxSplits ? ckv::kMaxSplits : splits);
   x.n_splits = splits;
   x.pages_per_split = x.kmax > 0 ? (x.kmax + splits - 1) / splits : 1;
@@ -216,6 +218,7 @@ bool plan_fused(ckv::Shape* s, hipStream_t stream, bool probe) {
   in.page_limit = 1 << ckv::kFusedPageBits;
   in.pairs = s->B * s->Hkv;
   in.xcds = 0;
+  in.max_rounds = ckv::kFusedMaxRounds;
   // the shape rules first, so that a shape that never fuses queries nothing
   in.resident = 1 << 30;
   if (!ckv::plan::single_launch(in).single) return false;

@@ -13,12 +13,16 @@ constexpr int kChunk = 256;         // blocks scored by one scan workgroup
 constexpr int kSlice = 1024;        // blocks ranked by one select workgroup
 constexpr int kGatherPages = 4;     // selected blocks per gather workgroup (unfused path)
 constexpr int kMaxSplits = 64;      // gather workgroups per (sequence, KV head), unfused path
+constexpr int kGatherGroups = 512;  // gather workgroups of one attend launch at most (two per CU of
+                                    //   MI355X): more would run in rounds of dependent loads
 constexpr int kDensePages = 128;    // blocks per dense workgroup
 constexpr int kMaxBlocks = 15872;   // blocks per sequence (page-table width)
 constexpr int kMaxKvHeads = 64;
 constexpr int kMergeFactors = 4096; // LDS floats for merge factors: G * (chunks + 2 * parts)
 constexpr int kCandLds = 2048;      // second-level candidates kept in LDS (else read from memory)
 constexpr int kShareMax = 256;      // selected blocks one fused workgroup attends to
+constexpr int kFusedMaxRounds = 2;  // rounds of pairs the single launch takes at most (measured: at
+                                    //   three rounds and more the three launches are faster)
 constexpr int kMaxChunks = (kMaxBlocks + kChunk - 1) / kChunk;
 constexpr int kFusedCand = 4608;    // fused step: candidates of all chunks held in LDS
 constexpr int kFusedPageBits = 18;  // fused step: page ids carried in selection keys (P < 2^18)

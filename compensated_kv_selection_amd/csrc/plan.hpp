@@ -38,6 +38,7 @@ struct Inputs {
   int resident;     // workgroups of the kernel resident on the device at once
   int pairs;        // (sequence, KV head) pairs of the call
   int xcds;         // > 0: the device sends workgroup i to XCD i % xcds; 0: unknown / not so
+  int max_rounds;   // rounds of pairs beyond which the three launches are faster
 };
 
 struct Layout {
@@ -49,15 +50,17 @@ struct Layout {
 
 // One launch when its whole grid - at least the control workgroups of every
 // chunk of one pair and a value workgroup per four chunks - can be resident
-// at once, the pair's candidates fit in shared memory and page ids fit in its
-// selection keys.  Keeping every pair on one XCD is preferred when it takes
-// no more rounds than spreading them.
+// at once, the pairs take at most max_rounds rounds of it, the pair's
+// candidates fit in shared memory and page ids fit in its selection keys.
+// (Every round is a full chain of dependent hand-offs; the three launches
+// stream all pairs at once instead.)  Keeping every pair on one XCD is
+// preferred when it takes no more rounds than spreading them.
 inline Layout single_launch(const Inputs& in) {
   Layout out;
   if (in.share > in.share_max || in.n_chunks * in.kmax > in.cand_max) return out;
   if (in.num_pages >= in.page_limit) return out;
   const Fit spread = fit_pairs(in.n_chunks, in.resident, in.pairs);
-  if (spread.rounds == 0) return out;
+  if (spread.rounds == 0 || spread.rounds > in.max_rounds) return out;
   out.single = true;
   out.n_val = spread.n_val;
   out.bg_round = spread.per_round;

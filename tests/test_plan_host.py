@@ -30,9 +30,9 @@ def driver(tmp_path_factory):
     return run
 
 
-def case(n_chunks, kmax, pairs, resident=512, xcds=8, share=None, num_pages=8192):
+def case(n_chunks, kmax, pairs, resident=512, xcds=8, share=None, num_pages=8192, max_rounds=1000):
     share = share if share is not None else max(1, -(-kmax // n_chunks)) if kmax else 1
-    return (n_chunks, kmax, share, SHARE_MAX, CAND_MAX, num_pages, PAGE_LIMIT, resident, pairs, xcds)
+    return (n_chunks, kmax, share, SHARE_MAX, CAND_MAX, num_pages, PAGE_LIMIT, resident, pairs, xcds, max_rounds)
 
 
 def rounds_of(n_chunks, n_val, per_round, pairs):
@@ -89,3 +89,13 @@ def test_every_single_launch_fits_and_takes_the_fewest_rounds(driver):
         best = min(-(-pairs // min(pairs, resident // (n_chunks + nv))) for nv in feasible)
         assert rounds_of(n_chunks, n_val, bg_round, pairs) == best, c
     assert n_single > 100
+
+
+def test_more_rounds_than_allowed_take_three_launches(driver):
+    # 128K tokens (32 chunks) per pair on 512 resident slots: 8 pairs take one
+    # round, 16 two, 32 four; 16 sequences of 64K (16 chunks) and 8 KV heads
+    # (128 pairs) take six
+    got = driver([case(32, 32, 8, max_rounds=2), case(32, 32, 16, max_rounds=2),
+                  case(32, 32, 32, max_rounds=2), case(16, 64, 128, max_rounds=2)])
+    assert [g[0] for g in got] == [1, 1, 0, 0]
+    assert got[1][2] == 8  # two rounds of 8 pairs
