@@ -100,6 +100,9 @@ constexpr int kSurvRows = 32;              // survivors whose mean values are re
 struct OpUmax {
   __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
 };
+struct OpUmin {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
 
 // e^x and ln x through the hardware's base-2 instructions (v_exp_f32,
 // v_log_f32): within a few units in the last place, denormal results flushed
@@ -215,6 +218,24 @@ __device__ __forceinline__ void attend_rows(float (&m)[G], float (&l)[G], float 
   }
 }
 
+// cnt[u] += the number of keys in key[0..n) above si[u], u < NU (bits of
+// non-negative floats, which order like the values).  key is 16-byte
+// aligned and n a multiple of 8: the keys are read as LDS broadcasts, eight
+// at a time in two 16-byte reads.
+template <int NU>
+__device__ __forceinline__ void count_above(const float* key, int n, const uint32_t (&si)[4], int (&cnt)[4]) {
+  const float4* k4 = reinterpret_cast<const float4*>(key);
+  for (int j = 0; j < n / 4; j += 2) {
+    const float4 a = k4[j], b = k4[j + 1];
+    const uint32_t sj[8] = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w),
+                            __float_as_uint(b.x), __float_as_uint(b.y), __float_as_uint(b.z), __float_as_uint(b.w)};
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) cnt[u] += sj[jj] > si[u] ? 1 : 0;
+  }
+}
+
 // Ranked score of a block from its G per-head log-scores lam[j * stride]:
 // sum over heads, in head order, of exp(lam_h - lnz_h), where lnz_h is log
 // Z_hat_h (or a part of it).  A published sample is scored with this same
@@ -255,6 +276,7 @@ struct CtlLds {
   uint32_t sh[64];
   uint32_t wsum[NW];
   uint32_t count;
+  uint32_t ccount;        // the pair's candidates counted into surv (zeroed at entry)
   float lzc[G];           // log of this chunk's part of Z_hat per head
   uint32_t tlo32;         // score bits of the lower bound of the pair's k-th ranked score
   uint64_t tsel;          // the pair's k-th largest key
@@ -347,6 +369,42 @@ __device__ void read_published(const Coh& src, int n, int per, int stride, uint6
         if (++spins == kPollLimit) st_c(err, 1u);
       }
       if (e < n) dst[e] = v[u];
+    }
+  }
+}
+
+// read_published for the pair's candidate words, which also gathers the
+// real ones (> 1) into list[0..63] in any order, counting them all in *count
+// (one shared-memory atomic per wave and batch).
+__device__ void read_candidates(const Coh& src, int n, int per, int stride, uint64_t* dst, uint64_t* list,
+                                uint32_t* count, uint32_t* err) {
+  const int t = threadIdx.x, lane = t & 63;
+  uint32_t spins = 0;
+  for (int base = 0; base < n; base += NT * kPollBatch) {
+    uint64_t v[kPollBatch];
+#pragma unroll
+    for (int u = 0; u < kPollBatch; ++u) {
+      const int e = base + t + u * NT;
+      v[u] = e < n ? src.u64((e / per) * stride + e % per) : 1u;
+    }
+#pragma unroll
+    for (int u = 0; u < kPollBatch; ++u) {
+      const int e = base + t + u * NT;
+      while (v[u] == 0 && spins < kPollLimit) {
+        __builtin_amdgcn_s_sleep(1);
+        v[u] = src.u64((e / per) * stride + e % per);
+        if (++spins == kPollLimit) st_c(err, 1u);
+      }
+      if (e < n) dst[e] = v[u];
+      const bool real = e < n && v[u] > 1u;
+      const uint64_t bal = __ballot(real);
+      if (bal) {  // uniform across the wave
+        uint32_t b0 = 0;
+        if (lane == 0) b0 = atomicAdd(count, (uint32_t)__popcll(bal));
+        b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)b0);
+        const uint32_t pos = b0 + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (real && pos < 64) list[pos] = v[u];
+      }
     }
   }
 }
@@ -594,6 +652,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     L.qsq[tid] = sq;
   }
   L.pgt[tid] = tid < nrows && pge >= 0 && pge < s.P ? pge : -1;
+  if (tid == 0) L.ccount = 0u;
   __syncthreads();
   // |q_h restricted to channel group t|^2, from the 8-channel partials when
   // a group spans whole partials
@@ -934,7 +993,10 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     const int nh = s.n_chunks * G;
     const int ns = sampled ? s.n_chunks * NW : 0;
     float* sml = reinterpret_cast<float*>(L.u.keys + nh);  // [ns][G] sample log-scores
-    float* sms = sml + ns * G;                               // [ns] their ranked scores
+    // their ranked scores, a quarter of the samples (n_chunks) per row of QP,
+    // zero padded, 16-byte aligned
+    const int QP = (s.n_chunks + 7) & ~7;
+    float* sms = reinterpret_cast<float*>(L.u.keys + ((nh + (ns * G + 1) / 2 + 1) & ~1));
     {
       const Coh hdr(hdr_half(s, w, tag) + (size_t)bg * nh, (size_t)nh * 8, s.n_xcd > 0);
       const Coh smp(w.fsmp + (size_t)bg * s.n_chunks * NW * G, (size_t)s.n_chunks * NW * G * 8, s.n_xcd > 0);
@@ -959,41 +1021,42 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     // ranked key of block tid of the chunk (nrows <= NT), and the samples' scores
     uint64_t mykey = 0;
     if (tid < nrows) mykey = fused_key(ranked_score<G>(&L.lam[0][tid], kChunk, L.lnz), start + tid, L.pgt[tid]);
-    if (tid < ns) sms[tid] = ranked_score<G>(sml + tid * G, 1, L.lnz);
+    const bool real_smp = sampled && tid < NW * QP && tid % QP < s.n_chunks;  // NW * QP <= NT
+    if (sampled && tid < NW * QP)
+      sms[tid] = real_smp ? ranked_score<G>(sml + ((tid / QP) * s.n_chunks + tid % QP) * G, 1, L.lnz) : 0.f;
     __syncthreads();
     CKV_MARK(chunk, 12);
     // The lower bound: the k-th largest sample score.  Each wave counts, for
-    // up to four samples per lane, the samples of its quarter of them that
+    // the samples in its lanes' slots, the samples of its row of QP that
     // score higher; the four counts are summed, and the smallest score with
     // fewer than k higher ones is the k-th largest (the score bits of
-    // non-negative floats order like the scores).
+    // non-negative floats order like the scores; the zero pads are above
+    // none and are not ranked).
     if (sampled) {
-      int* rkb = reinterpret_cast<int*>(sms + ns);  // [NW][256] partial counts
-      const int q0 = wave * ns / NW, q1 = (wave + 1) * ns / NW;
+      int* rkb = reinterpret_cast<int*>(sms + NW * QP);  // [NW][NT] partial counts
       uint32_t si[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) si[u] = lane + 64 * u < ns ? __float_as_uint(sms[lane + 64 * u]) : ~0u;
+      for (int u = 0; u < 4; ++u) {
+        const int e = lane + 64 * u;
+        si[u] = e < NW * QP && e % QP < s.n_chunks ? __float_as_uint(sms[e]) : ~0u;
+      }
       int cnt[4] = {0, 0, 0, 0};
       CKV_MARK(chunk, 22);
-      for (int j0 = q0; j0 < q1; j0 += 8) {
-        uint32_t sj[8];  // LDS broadcasts, requested together; 0 counts for none
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) sj[jj] = j0 + jj < q1 ? __float_as_uint(sms[j0 + jj]) : 0u;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) cnt[u] += sj[jj] > si[u] ? 1 : 0;
-      }
+      if (NW * QP <= 128) count_above<2>(sms + wave * QP, QP, si, cnt);
+      else count_above<4>(sms + wave * QP, QP, si, cnt);
       CKV_MARK(chunk, 23);
 #pragma unroll
       for (int u = 0; u < 4; ++u) rkb[wave * NT + lane + 64 * u] = cnt[u];
       if (tid == 0) L.tlo32 = ns >= kk ? ~0u : 0u;
       __syncthreads();
       CKV_MARK(chunk, 24);
-      if (tid < ns && ns >= kk) {
+      uint32_t lo = ~0u;
+      if (real_smp && ns >= kk) {
         const int r = rkb[tid] + rkb[NT + tid] + rkb[2 * NT + tid] + rkb[3 * NT + tid];
-        if (r < kk) atomicMin(&L.tlo32, __float_as_uint(sms[tid]));
+        if (r < kk) lo = __float_as_uint(sms[tid]);
       }
+      lo = wave_reduce(lo, OpUmin{});  // one shared-memory atomic per wave
+      if (lane == 0 && lo != ~0u) atomicMin(&L.tlo32, lo);
     }
     __syncthreads();
     CKV_MARK(chunk, 13);
@@ -1042,7 +1105,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       for (int e = k1 + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);  // below every real key
     }
     __syncthreads();
-    if (tid == 0) L.count = 0u;  // ordered before the candidates' count by the wait below
     CKV_MARK(chunk, 5);
     if (n_pv > 0) {
       // rows of the first survivors (row slot rs, slice c), requested now
@@ -1064,26 +1126,12 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       }
       if (rs < n_pv) raw_load(mv + (size_t)L.srow[rs] * D + c * 8, pnv);  // for the take-back
     }
-    // the pair's candidates
+    // the pair's candidates, the real ones gathered into L.surv
     const int n2 = s.n_chunks * kk;
-    read_published(cand, n2, kk, s.kmax, L.u.keys, err);
+    read_candidates(cand, n2, kk, s.kmax, L.u.keys, L.surv, &L.ccount, err);
     __syncthreads();
     CKV_MARK(chunk, 6);
-    for (int e0 = wave * 64; e0 < n2; e0 += NT) {  // wave-uniform bounds
-      const int e = e0 + lane;
-      const uint64_t key = e < n2 ? L.u.keys[e] : 0ull;
-      const bool real = key > 1u;
-      const uint64_t bal = __ballot(real);
-      if (bal) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&L.count, (uint32_t)__popcll(bal));
-        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-        const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        if (real && pos < 64) L.surv[pos] = key;
-      }
-    }
-    __syncthreads();
-    const uint32_t ncand = L.count;
+    const uint32_t ncand = L.ccount;
     uint64_t T;
     CKV_MARK(chunk, 14);
     if (kk <= kFastK && ncand <= 64) {
@@ -1292,7 +1340,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         } else if (wave == 0) {
           // by ascending block index: a selected block's place is the number
           // of selected blocks with a lower index
-          const uint32_t ncand = L.count;
+          const uint32_t ncand = L.ccount;
           const uint64_t T = L.tsel;
           const uint64_t mine = lane < (int)ncand ? L.surv[lane] : 0ull;
           const bool chosen = lane < (int)ncand && mine >= T;
