@@ -104,11 +104,6 @@ struct OpUmin {
   __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
 };
 
-// e^x and ln x through the hardware's base-2 instructions (v_exp_f32,
-// v_log_f32): within a few units in the last place, denormal results flushed
-// to zero.
-__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
-__device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
 // exp(a - m), 0 for an empty state (a = -inf)
 __device__ __forceinline__ float fscale(float a, float m) { return a == -INFINITY ? 0.f : fexp(a - m); }
 
@@ -275,7 +270,6 @@ struct CtlLds {
   int gpg[kShareMax];
   uint32_t sh[64];
   uint32_t wsum[NW];
-  uint32_t count;
   uint32_t ccount;        // the pair's candidates counted into surv (zeroed at entry)
   float lzc[G];           // log of this chunk's part of Z_hat per head
   uint32_t tlo32;         // score bits of the lower bound of the pair's k-th ranked score
@@ -284,6 +278,7 @@ struct CtlLds {
   int rk[NW][64];         // their ranks, counted by quarters
   uint32_t wsum2[NW];
   uint32_t wsum3[NW];
+  uint32_t wcnt[NW];      // selected candidates per wave's range of the candidate array
   int srow[kSurvRows];          // rows of the first survivors, whose mean values (and the first
                                 // kPrefetchBlocks' rows) were requested early
   uint32_t ssel[kPrefetchBlocks];  // whether each survivor with requested rows was selected
@@ -1089,18 +1084,21 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       n_pf = min(n_s, NPB);
       n_pv = min(n_s, RS);
     } else {
-      // the chunk's top-k candidates by a radix selection, in any order
+      // the chunk's top-k candidates by a radix selection, in row order (the
+      // order is the same in every call: the shared-out gather follows it)
       const int k1 = min(kk, nrows);
       if (tid < nrows) L.u.keys[tid] = mykey;
       __syncthreads();
       if (k1 > 0) {
         const uint64_t T1 = k1 == nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
-        if (tid == 0) L.count = 0u;
+        const bool top = tid < nrows && mykey >= T1;  // nrows <= NT
+        const uint64_t bt = __ballot(top);
+        if (lane == 0) L.wcnt[wave] = (uint32_t)__popcll(bt);
         __syncthreads();
-        for (int i = tid; i < nrows; i += NT) {
-          const uint64_t key = L.u.keys[i];
-          if (key >= T1) cand.put_u64(chunk * s.kmax + (int)atomicAdd(&L.count, 1u), key);
-        }
+        int pos = (int)__popcll(bt & ((1ull << lane) - 1ull));
+#pragma unroll
+        for (int v = 0; v < NW; ++v) pos += v < wave ? (int)L.wcnt[v] : 0;
+        if (top) cand.put_u64(chunk * s.kmax + pos, mykey);
       }
       for (int e = k1 + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);  // below every real key
     }
@@ -1179,11 +1177,13 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
     // this chunk's selected blocks (keys >= T), in row order: for the
     // take-back, those whose mean value was not requested early; for the
-    // gather, those whose rows were not
+    // gather, those whose rows were not (without samples, the same for every
+    // chunk of the pair, the gather is shared out evenly below instead)
+    const bool spread = !sampled;
     const bool sel = tid < nrows && mykey >= T;
     const bool in_pf = sel && pf && spos < n_pf;
     const bool in_pv = sel && pf && spos < n_pv;
-    const uint64_t bsel = __ballot(sel && !in_pv), bgat = __ballot(sel && !in_pf), btb = __ballot(in_pv);
+    const uint64_t bsel = __ballot(sel && !in_pv), bgat = __ballot(sel && !in_pf && !spread), btb = __ballot(in_pv);
     if (lane == 0) {
       L.wsum[wave] = (uint32_t)__popcll(bsel);
       L.wsum2[wave] = (uint32_t)__popcll(bgat);
@@ -1204,9 +1204,51 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     if (sel && !in_pv) L.own[opos] = tid;
     if (in_pf) L.ssel[spos] = 1u;
     if (in_pv) L.tbk[spos] = 1u;
-    if (sel && !in_pf) {
+    if (sel && !in_pf && !spread) {
       L.gblk[gpos] = start + tid;
       L.gpg[gpos] = L.pgt[tid];
+    }
+    if (spread) {
+      // The pair's selected blocks shared out evenly: the p-th of them (in
+      // the order below) to chunk p mod n_chunks.  Each wave takes a range
+      // of the candidate array, two entries per lane in one 16-byte read;
+      // it counts its selected entries, then places them after the earlier
+      // waves'.
+      const int per_w = ((n2 + NW - 1) / NW + 127) & ~127;
+      const int e_lo = min(n2, wave * per_w), e_hi = min(n2, e_lo + per_w);
+      const uint4* k4 = reinterpret_cast<const uint4*>(L.u.keys);  // e_lo even: 16-byte pairs
+      const uint64_t lt = (1ull << lane) - 1ull;
+      int cw = 0;
+      for (int e0 = e_lo; e0 < e_hi; e0 += 128) {
+        const int e = e0 + 2 * lane;
+        const uint4 v = e < e_hi ? k4[e >> 1] : make_uint4(0u, 0u, 0u, 0u);
+        const bool sa = e < e_hi && (((uint64_t)v.y << 32) | v.x) >= T;
+        const bool sb = e + 1 < e_hi && (((uint64_t)v.w << 32) | v.z) >= T;
+        cw += (int)(__popcll(__ballot(sa)) + __popcll(__ballot(sb)));
+      }
+      if (lane == 0) L.wcnt[wave] = (uint32_t)cw;
+      __syncthreads();
+      int p0 = 0;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) p0 += v < wave ? (int)L.wcnt[v] : 0;
+      for (int e0 = e_lo; e0 < e_hi; e0 += 128) {
+        const int e = e0 + 2 * lane;
+        const uint4 v = e < e_hi ? k4[e >> 1] : make_uint4(0u, 0u, 0u, 0u);
+        const uint64_t ka = ((uint64_t)v.y << 32) | v.x, kb = ((uint64_t)v.w << 32) | v.z;
+        const bool sa = e < e_hi && ka >= T, sb = e + 1 < e_hi && kb >= T;
+        const uint64_t ba = __ballot(sa), bb = __ballot(sb);
+        const int pa = p0 + (int)(__popcll(ba & lt) + __popcll(bb & lt)), pb = pa + (sa ? 1 : 0);
+        if (sa && pa % s.n_chunks == chunk && pa < kk) {
+          L.gblk[pa / s.n_chunks] = fused_key_index(ka);
+          L.gpg[pa / s.n_chunks] = fused_key_page(ka);
+        }
+        if (sb && pb % s.n_chunks == chunk && pb < kk) {
+          L.gblk[pb / s.n_chunks] = fused_key_index(kb);
+          L.gpg[pb / s.n_chunks] = fused_key_page(kb);
+        }
+        p0 += (int)(__popcll(ba) + __popcll(bb));
+      }
+      n_gather = chunk < kk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
     }
     __syncthreads();
     CKV_MARK(chunk, 7);

@@ -341,7 +341,7 @@ __device__ void scan_role(const Shape& s, const StepIO& io, const Work& w, int t
         const int n = min(s.bs, Lseq - (start + ri) * s.bs);
         const float sb = L.sb[j][ri], half = 0.5f * L.vh[j][ri];
         const float massf = (float)n * (1.f + half);  // second-order mass estimate / e^{s_bar}
-        lamv[u] = io.score_mode == kScoreMass ? sb + logf(massf) : sb + logf(massf * half);
+        lamv[u] = io.score_mode == kScoreMass ? sb + flog(massf) : sb + flog(massf * half);
         mx = fmaxf(mx, sb);
         cx = fmaxf(cx, lamv[u]);
       }
@@ -355,11 +355,11 @@ __device__ void scan_role(const Shape& s, const StepIO& io, const Work& w, int t
       const int ri = lane + 64 * u;
       if (ri < nrows) {
         const int n = min(s.bs, Lseq - (start + ri) * s.bs);
-        const float wt = (float)n * expf(L.sb[j][ri] - mx);
+        const float wt = (float)n * fexp(L.sb[j][ri] - mx);
         lsum += wt;
         zsum = fmaf(wt, 1.f + 0.5f * L.vh[j][ri], zsum);
         L.w[j][ri] = wt;
-        xrow[ri] = lamv[u] == -INFINITY ? 0.f : expf(lamv[u] - cx);
+        xrow[ri] = lamv[u] == -INFINITY ? 0.f : fexp(lamv[u] - cx);
       }
     }
     lsum = wave_sum(lsum);

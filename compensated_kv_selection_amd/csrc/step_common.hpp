@@ -22,6 +22,12 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// e^x and ln x through the hardware's base-2 instructions (v_exp_f32,
+// v_log_f32): within a few units in the last place, denormal results flushed
+// to zero.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+
 // ---- coherent access to workspace written inside the same launch -----------
 // The XCDs of the device have separate L2 caches.  Words that one workgroup
 // writes and another reads during the same launch are written and read with
