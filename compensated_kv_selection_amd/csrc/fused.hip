@@ -20,33 +20,32 @@
 //   a control workgroup loads the chunk's mean keys, grouped variances and
 //     page-table entries, computes the block-mean logits on the matrix cores
 //     (the G query heads are the rows of a 16x16x32 bf16 MFMA tile),
-//     publishes the chunk's compensation weights, its header (max logit and
-//     partial Z_hat per head) and four samples (the per-head log-scores of
-//     each wave's best block by the chunk's own Z_hat part); reads every
-//     header and sample of the pair, scores its blocks and the samples, and
-//     takes the k-th largest sample score as a lower bound of the pair's
-//     k-th score; publishes its blocks at or above the bound (the survivors,
-//     about k + 10 per pair) as candidates and requests the first survivors'
-//     keys and values at once; reads every candidate of the pair and ranks
-//     them to find the pair's k-th key T; attends exactly to its own blocks
-//     with keys >= T, takes back their compensation terms and publishes one
-//     (max, sum, acc[d]) partial per query head;
-//   a value workgroup (bf16: requesting the chunk's mean values on entry)
-//     waits for the chunk's weights, sums the compensation terms of all the
-//     chunk's blocks and publishes them as a partial of its own.
+//     publishes the chunk's compensation weights and header (max logit,
+//     partial Z_hat per head), reads every header of the pair, ranks the
+//     chunk's blocks, publishes the chunk's top-k candidates, reads every
+//     candidate of the pair, finds the pair's top-k, attends exactly to its
+//     share of the selected blocks (ranks chunk, chunk + n_chunks, ... of the
+//     pair's selection), takes back the compensation terms of the selected
+//     blocks of its chunk, folds in the chunk's value sums and publishes
+//     one (max, sum, acc[d]) partial per query head;
+//   a value workgroup waits for a chunk's weights, streams the chunk's mean
+//     values, sums the compensation terms of all the chunk's blocks and
+//     publishes them for the chunk's control workgroup.
 // Then every control workgroup of the pair merges its slice of the pair's
-// output from the pair's control and value partials, and chunk 0's advances
-// the pair's epoch.
+// output from the control workgroups' partials, and chunk 0's advances the
+// pair's epoch.
 // A wave's memory counter drains in issue order, so the long mean-value
-// stream lives in workgroups that never wait on small hand-offs.
+// stream lives in workgroups that never wait on small hand-offs; it starts
+// once the mean keys have arrived, so that the ranking does not wait behind
+// it, and it is paced, so that it does not slow the hand-offs.
 // Hand-offs are 64-bit words read with device-scope loads: headers and
 // candidates are never 0 once written (double-buffered by the parity of the
 // call's tag, each half cleared during the call after the one that used it);
-// weights, samples and partials carry the call's tag in their upper half.
-// Readers poll such words directly, so publishing needs no completion wait.
-// When the device sends workgroups to its XCDs in turn, all workgroups of a
-// pair run on one XCD and the words are stored with the default policy, so
-// they are handed over in that XCD's L2; otherwise they are written through.
+// weights and partials carry the call's tag in their upper half.  Readers poll such
+// words directly, so publishing needs no completion wait.  When the device
+// sends workgroups to its XCDs round robin, all workgroups of a pair run on
+// one XCD and the words are stored with the default policy, so they are
+// handed over in that XCD's L2; otherwise they are written through.
 //
 // The grid covers bg_round pairs at once and walks the rest in rounds; the
 // host launches it only when the whole grid can be resident, so the
@@ -63,19 +62,6 @@ namespace {
 
 constexpr int NT = 256;                    // threads per workgroup
 constexpr int NW = NT / 64;                // waves per workgroup
-constexpr int kPollBatch = 8;              // published words read per thread per round trip
-constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
-constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
-constexpr int kXccProbeBlocks = 256;       // workgroups of the XCD placement check
-constexpr uint32_t kErrPlacement = 2u;     // error word: a workgroup ran on an XCD the placement check did not see
-constexpr uint32_t kErrSelect = 4u;        // error word: fewer candidates than selected blocks (never expected)
-constexpr int kFastK = 64;                 // selections of at most one wave's width: sampled lower bound,
-                                           //   ranking of the pair's candidates in one wave
-constexpr int kPrefetch = 4;               // register slots for survivors' rows requested before the
-                                           //   selection is known (16 row slots each at d = 128)
-constexpr int kPrefetchBlocks = 8;         // survivors those slots can cover (d = 64: 32 row slots)
-constexpr int kSurvRows = 32;              // survivors whose mean values are requested early (row slots)
-
 #ifdef CKV_PHASE_TRACE
 // Phase trace, compiled only into a separately built library for timing
 // studies: thread 0 of a workgroup stores the constant-rate clock at mark i
@@ -97,154 +83,11 @@ constexpr int kSurvRows = 32;              // survivors whose mean values are re
 #define CKV_MARK(slot, i) CKV_NOTE(slot, i, 0)
 #endif
 
-struct OpUmax {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
-};
-struct OpUmin {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
-};
-
-// exp(a - m), 0 for an empty state (a = -inf)
-__device__ __forceinline__ float fscale(float a, float m) { return a == -INFINITY ? 0.f : fexp(a - m); }
-
-// Online softmax update of one query head's state with one logit (value
-// slice val), with the fast exponential.
-template <int G>
-__device__ __forceinline__ void online_step(float (&m)[G], float (&l)[G], float (&acc)[G][8], int j, float logit,
-                                            const float (&val)[8]) {
-  if (logit > m[j]) {
-    const float sc = fscale(m[j], logit);
-    l[j] *= sc;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] *= sc;
-    m[j] = logit;
-  }
-  const float p = fexp(logit - m[j]);
-  l[j] += p;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, val[e], acc[j][e]);
-}
-
-// This thread's 8-channel slice of the G query rows, as the dot products
-// with a key slice want it: bf16 pairs for bf16 keys (multiplied exactly,
-// summed in fp32 by v_dot2), fp32 otherwise.
-template <typename KV, int G> struct QSlice;
-template <int G> struct QSlice<uint16_t, G> {
-  uint32_t p[G][4];
-  __device__ __forceinline__ void set(const float* qf, int D, int c) {
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)  // the floats hold bf16 values: their upper halves are the bf16 bits
-        p[j][e] = (__float_as_uint(qf[j * D + c * 8 + 2 * e]) >> 16) |
-                  (__float_as_uint(qf[j * D + c * 8 + 2 * e + 1]) & 0xFFFF0000u);
-  }
-  __device__ __forceinline__ void dot(const Raw8<uint16_t>& k, float (&d)[G]) const {
-    const uint32_t kw[4] = {k.a.x, k.a.y, k.a.z, k.a.w};
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float a = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw[e]), __builtin_bit_cast(bf16x2_t, p[j][e]),
-                                            a, false);
-      d[j] = a;
-    }
-  }
-};
-template <int G> struct QSlice<float, G> {
-  float q[G][8];
-  __device__ __forceinline__ void set(const float* qf, int D, int c) {
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[j][e] = qf[j * D + c * 8 + e];
-  }
-  __device__ __forceinline__ void dot(const Raw8<float>& k, float (&d)[G]) const {
-    float x[8];
-    raw_float(k, x);
-    dot8<G>(q, x, d);
-  }
-};
-
-// Exact attention to up to N token rows (row slot u in use on every lane of
-// its row, or on none): the logits of all of them first, then one online
-// update per head, so that the state's max moves once per batch.
-template <typename KV, int G, int LPR, int N>
-__device__ __forceinline__ void attend_rows(float (&m)[G], float (&l)[G], float (&acc)[G][8], const QSlice<KV, G>& q,
-                                            const Raw8<KV> (&kr)[N], const Raw8<KV> (&vr)[N], const bool (&use)[N],
-                                            float tau) {
-  float x[N][G], mn[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) mn[j] = m[j];
-#pragma unroll
-  for (int u = 0; u < N; ++u) {
-    if (use[u]) {
-      float d[G];
-      q.dot(kr[u], d);
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        x[u][j] = token_row_sum<LPR>(d[j]) * tau;
-        mn[j] = fmaxf(mn[j], x[u][j]);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float sc = fscale(m[j], mn[j]);
-    l[j] *= sc;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] *= sc;
-    m[j] = mn[j];
-  }
-#pragma unroll
-  for (int u = 0; u < N; ++u) {
-    if (use[u]) {
-      float v8[8];
-      raw_float(vr[u], v8);
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float p = fexp(x[u][j] - m[j]);
-        l[j] += p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, v8[e], acc[j][e]);
-      }
-    }
-  }
-}
-
-// cnt[u] += the number of keys in key[0..n) above si[u], u < NU (bits of
-// non-negative floats, which order like the values).  key is 16-byte
-// aligned and n a multiple of 8: the keys are read as LDS broadcasts, eight
-// at a time in two 16-byte reads.
-template <int NU>
-__device__ __forceinline__ void count_above(const float* key, int n, const uint32_t (&si)[4], int (&cnt)[4]) {
-  const float4* k4 = reinterpret_cast<const float4*>(key);
-  for (int j = 0; j < n / 4; j += 2) {
-    const float4 a = k4[j], b = k4[j + 1];
-    const uint32_t sj[8] = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w),
-                            __float_as_uint(b.x), __float_as_uint(b.y), __float_as_uint(b.z), __float_as_uint(b.w)};
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) cnt[u] += sj[jj] > si[u] ? 1 : 0;
-  }
-}
-
-// Ranked score of a block from its G per-head log-scores lam[j * stride]:
-// sum over heads, in head order, of exp(lam_h - lnz_h), where lnz_h is log
-// Z_hat_h (or a part of it).  A published sample is scored with this same
-// function on the same bits as the block's own chunk scores it.
-template <int G>
-__device__ __forceinline__ float ranked_score(const float* lam, int stride, const float* lnz) {
-  float S = 0.f;
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float a = lam[j * stride], lz = lnz[j];
-    if (a != -INFINITY && lz != -INFINITY) S += fexp(a - lz);
-  }
-  return S;
-}
+constexpr int kPollBatch = 8;              // published words read per thread per round trip
+constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
+constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
+constexpr int kXccProbeBlocks = 256;       // workgroups of the XCD placement check
+constexpr uint32_t kErrPlacement = 2u;     // error word: a workgroup ran on an XCD it was not placed on
 
 template <int D, int G>
 struct CtlLds {
@@ -270,19 +113,10 @@ struct CtlLds {
   int gpg[kShareMax];
   uint32_t sh[64];
   uint32_t wsum[NW];
-  uint32_t ccount;        // the pair's candidates counted into surv (zeroed at entry)
-  float lzc[G];           // log of this chunk's part of Z_hat per head
-  uint32_t tlo32;         // score bits of the lower bound of the pair's k-th ranked score
-  uint64_t tsel;          // the pair's k-th largest key
-  uint64_t surv[64];      // the pair's candidates (when at most 64)
-  int rk[NW][64];         // their ranks, counted by quarters
-  uint32_t wsum2[NW];
-  uint32_t wsum3[NW];
-  uint32_t wcnt[NW];      // selected candidates per wave's range of the candidate array
-  int srow[kSurvRows];          // rows of the first survivors, whose mean values (and the first
-                                // kPrefetchBlocks' rows) were requested early
-  uint32_t ssel[kPrefetchBlocks];  // whether each survivor with requested rows was selected
-  uint32_t tbk[kSurvRows];         // whether each survivor with a requested mean value was selected
+  uint32_t count;
+  uint64_t tlo;           // lower bound of the pair's k-th largest candidate
+  uint64_t surv[64];      // candidates at or above it
+  uint32_t nown;          // selected blocks of this chunk
   uint4 tmk[D / 8];       // decode append: the tail block's new mean key (stored bits),
   float tgv[4];           //   its grouped variances (r = 4)
   float tmv[D];           //   and its new mean value as stored
@@ -368,78 +202,6 @@ __device__ void read_published(const Coh& src, int n, int per, int stride, uint6
   }
 }
 
-// read_published for the pair's candidate words, which also gathers the
-// real ones (> 1) into list[0..63] in any order, counting them all in *count
-// (one shared-memory atomic per wave and batch).
-__device__ void read_candidates(const Coh& src, int n, int per, int stride, uint64_t* dst, uint64_t* list,
-                                uint32_t* count, uint32_t* err) {
-  const int t = threadIdx.x, lane = t & 63;
-  uint32_t spins = 0;
-  for (int base = 0; base < n; base += NT * kPollBatch) {
-    uint64_t v[kPollBatch];
-#pragma unroll
-    for (int u = 0; u < kPollBatch; ++u) {
-      const int e = base + t + u * NT;
-      v[u] = e < n ? src.u64((e / per) * stride + e % per) : 1u;
-    }
-#pragma unroll
-    for (int u = 0; u < kPollBatch; ++u) {
-      const int e = base + t + u * NT;
-      while (v[u] == 0 && spins < kPollLimit) {
-        __builtin_amdgcn_s_sleep(1);
-        v[u] = src.u64((e / per) * stride + e % per);
-        if (++spins == kPollLimit) st_c(err, 1u);
-      }
-      if (e < n) dst[e] = v[u];
-      const bool real = e < n && v[u] > 1u;
-      const uint64_t bal = __ballot(real);
-      if (bal) {  // uniform across the wave
-        uint32_t b0 = 0;
-        if (lane == 0) b0 = atomicAdd(count, (uint32_t)__popcll(bal));
-        b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)b0);
-        const uint32_t pos = b0 + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        if (real && pos < 64) list[pos] = v[u];
-      }
-    }
-  }
-}
-
-// Wait until word i of src carries this call's tag; returns its float.
-__device__ __forceinline__ float read_tagged(const Coh& src, int i, uint64_t v, uint32_t tag, uint32_t& spins,
-                                             uint32_t* err);
-
-// Copy the pair's nh chunk-header words (nonzero once written) to hdr_dst
-// and ns tagged sample words (as floats) to smp_dst, waiting for each; every
-// request of a thread's batch is issued before its first wait.
-__device__ void read_headers_samples(const Coh& hdr, int nh, const Coh& smp, int ns, uint64_t* hdr_dst,
-                                     float* smp_dst, uint32_t tag, uint32_t* err) {
-  const int t = threadIdx.x;
-  const int n = nh + ns;
-  uint32_t spins = 0;
-  for (int base = 0; base < n; base += NT * kPollBatch) {
-    uint64_t v[kPollBatch];
-#pragma unroll
-    for (int u = 0; u < kPollBatch; ++u) {
-      const int e = base + t + u * NT;
-      v[u] = e < nh ? hdr.u64(e) : (e < n ? smp.u64(e - nh) : 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < kPollBatch; ++u) {
-      const int e = base + t + u * NT;
-      if (e < nh) {
-        while (v[u] == 0 && spins < kPollLimit) {
-          __builtin_amdgcn_s_sleep(1);
-          v[u] = hdr.u64(e);
-          if (++spins == kPollLimit) st_c(err, 1u);
-        }
-        hdr_dst[e] = v[u];
-      } else if (e < n) {
-        smp_dst[e - nh] = read_tagged(smp, e - nh, v[u], tag, spins, err);
-      }
-    }
-  }
-}
-
 // Wait until word i of src carries this call's tag; returns its float.
 __device__ __forceinline__ float read_tagged(const Coh& src, int i, uint64_t v, uint32_t tag, uint32_t& spins,
                                              uint32_t* err) {
@@ -476,7 +238,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
     uint32_t mb = __float_as_uint(m[j]);
     if (LPR == 8) mb = OpFmax{}(mb, dpp_row_ror8(mb));
     const float mw = __uint_as_float(across_rows(mb, OpFmax{}));
-    const float f = fscale(m[j], mw);
+    const float f = scale_from(m[j], mw);
     uint32_t lb = __float_as_uint(l[j] * f);
     if (LPR == 8) lb = OpFadd{}(lb, dpp_row_ror8(lb));
     const float lw = __uint_as_float(across_rows(lb, OpFadd{}));
@@ -507,7 +269,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
       const float* rw = red[v][j];
-      const float f = fscale(rw[0], Mx);
+      const float f = scale_from(rw[0], Mx);
       a0 = fmaf(rw[4 + 2 * d2], f, a0);
       a1 = fmaf(rw[4 + 2 * d2 + 1], f, a1);
       Ls = fmaf(rw[1], f, Ls);
@@ -522,7 +284,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
       const float le = read_tagged(*extra, h + 1, w1, tag, spins, err);
       const float e0 = read_tagged(*extra, h + 2 + 2 * d2, w2, tag, spins, err);
       const float e1 = read_tagged(*extra, h + 3 + 2 * d2, w3, tag, spins, err);
-      const float M = fmaxf(Mx, me), f1 = fscale(Mx, M), f2 = fscale(me, M);
+      const float M = fmaxf(Mx, me), f1 = scale_from(Mx, M), f2 = scale_from(me, M);
       a0 = a0 * f1 + e0 * f2;
       a1 = a1 * f1 + e1 * f2;
       Ls = Ls * f1 + le * f2;
@@ -559,8 +321,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   const int start = chunk * kChunk;
   const int nrows = max(0, min(M, start + kChunk) - start);
   const size_t row0 = (size_t)bg * s.max_blocks + start;  // logical summary row of the chunk
-  CKV_MARK(chunk, 0);
-  CKV_NOTE(chunk, 25, __builtin_amdgcn_s_memtime());
   const KV* mk = static_cast<const KV*>(io.summ.mean_k) + row0 * D;
   const KV* mv = static_cast<const KV*>(io.summ.mean_v) + row0 * D;
   const int r = s.r, gs = D / r;
@@ -582,6 +342,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
   }
 
+  CKV_MARK(chunk, 0);
+  CKV_NOTE(chunk, 25, __builtin_amdgcn_s_memtime());
   // ---- loads, all issued at once, oldest first: q, page-table entries, the
   // matrix-operand rows of q, then the chunk's mean keys and variances.
   // Buffer views end at the chunk's last block, so rows past it read 0. ----
@@ -647,7 +409,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     L.qsq[tid] = sq;
   }
   L.pgt[tid] = tid < nrows && pge >= 0 && pge < s.P ? pge : -1;
-  if (tid == 0) L.ccount = 0u;
   __syncthreads();
   // |q_h restricted to channel group t|^2, from the 8-channel partials when
   // a group spans whole partials
@@ -922,16 +683,15 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         const int n = min(s.bs, Lseq - (start + ri) * s.bs);
         const float sb = L.sb[j][ri], half = 0.5f * L.lam[j][ri];
         const float massf = (float)n * (1.f + half);  // second-order mass estimate / e^{s_bar}
-        const float wt = (float)n * fexp(sb - mx);
+        const float wt = (float)n * expf(sb - mx);
         z = fmaf(wt, 1.f + half, z);
         L.wt[j][ri] = wt;
-        L.lam[j][ri] = io.score_mode == kScoreMass ? sb + flog(massf) : sb + flog(massf * half);
+        L.lam[j][ri] = io.score_mode == kScoreMass ? sb + logf(massf) : sb + logf(massf * half);
         if (comp) wts.put_u64(j * kWStride + ri, tagged(wt, tag));
       }
       z = wave_sum_dpp(z);
       if (lane == 0) {
         L.mx[j] = mx;
-        L.lzc[j] = z > 0.f ? mx + flog(z) : -INFINITY;  // log of this chunk's part of Z_hat
         if (ranked) hdr.put_u64(chunk * G + j, ((uint64_t)__float_as_uint(z) << 32) | __float_as_uint(mx));
         if constexpr (kApp) {
           // decode append: wave 0 stored the new summary row; it is in L2
@@ -945,57 +705,16 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   __syncthreads();
   CKV_MARK(chunk, 3);
 
-  // ---- samples for the pair's lower bound of the k-th ranked score.  Each
-  // wave publishes the per-head log-scores of its block with the largest
-  // score by this chunk's own Z_hat part (a stand-in for the pair's, which is
-  // not known yet).  Any k distinct blocks' ranked scores bound the pair's
-  // k-th largest from below; the samples are scored later with the same
-  // arithmetic as the blocks themselves. ----
-  const bool sampled = ranked && kk <= kFastK && s.n_chunks * NW <= NT;  // at most NT samples
-  if (sampled) {
-    float p = 0.f;
-    if (tid < nrows) p = ranked_score<G>(&L.lam[0][tid], kChunk, L.lzc);
-    const uint32_t pb = tid < nrows ? __float_as_uint(p) : 0u;  // p >= 0: bits order like values
-    const uint32_t best = wave_reduce(pb, OpUmax{});
-    const uint64_t who = __ballot(pb == best);
-    const int row = 64 * wave + (int)__builtin_ctzll(who);
-    const Coh smp(w.fsmp + (size_t)bg * s.n_chunks * NW * G, (size_t)s.n_chunks * NW * G * 8, s.n_xcd > 0);
-    if (lane < G) smp.put_u64((chunk * NW + wave) * G + lane, tagged(row < nrows ? L.lam[lane][row] : -INFINITY, tag));
-  }
-
-  // ---- selection: the pair's k-th largest ranked key T; this chunk's
-  // selected blocks are its blocks with keys >= T, which it attends to ----
-  int n_own = 0, n_gather = 0, n_pf = 0, n_pv = 0, n_tb = 0;
-  bool listed = false;  // the pair's candidates fit one wave (ranked there; output from L.surv)
-  // Survivors of the lower bound, whose keys and values (and mean values)
-  // are requested before the pair's selection is known: their memory round
-  // trip then overlaps the candidate exchange.
-  // PF register slots per thread, as many as the registers allow; slot u of
-  // row slot rs holds token (u RS + rs) % 16 of survivor (u RS + rs) / 16, so
-  // the slots cover NPB survivors; thread rs also holds survivor rs's mean
-  // value slice (pnv).
-  constexpr int PF = G <= 4 && sizeof(KV) == 2 ? kPrefetch : (G <= 4 || kR4 ? kPrefetch / 2 : 0);
-  constexpr int NPB = PF * RS / kBlockSize;
-  static_assert(NPB <= kPrefetchBlocks, "prefetch bookkeeping");
-  static_assert(RS <= kSurvRows, "prefetch bookkeeping");
-  Raw8<KV> pk[PF > 0 ? PF : 1], pv[PF > 0 ? PF : 1], pnv;
-  bool pok[PF > 0 ? PF : 1];
-  pok[0] = false;
-#pragma unroll
-  for (int u = 0; u < PF; ++u) pok[u] = false;
+  // ---- selection: which blocks this workgroup attends to exactly, and
+  // which of the chunk's blocks were selected ----
+  int n_own = 0, n_gather = 0;
+  bool listed = false;  // selection list (and output) made by the one-wave path
   if (ranked) {
-    // log Z_hat per head from every chunk header of the pair, and the samples
+    // log Z_hat per head from every chunk header of the pair
     const int nh = s.n_chunks * G;
-    const int ns = sampled ? s.n_chunks * NW : 0;
-    float* sml = reinterpret_cast<float*>(L.u.keys + nh);  // [ns][G] sample log-scores
-    // their ranked scores, a quarter of the samples (n_chunks) per row of QP,
-    // zero padded, 16-byte aligned
-    const int QP = (s.n_chunks + 7) & ~7;
-    float* sms = reinterpret_cast<float*>(L.u.keys + ((nh + (ns * G + 1) / 2 + 1) & ~1));
     {
       const Coh hdr(hdr_half(s, w, tag) + (size_t)bg * nh, (size_t)nh * 8, s.n_xcd > 0);
-      const Coh smp(w.fsmp + (size_t)bg * s.n_chunks * NW * G, (size_t)s.n_chunks * NW * G * 8, s.n_xcd > 0);
-      read_headers_samples(hdr, nh, smp, ns * G, L.u.keys, sml, tag, err);
+      read_published(hdr, nh, nh, 0, L.u.keys, err);
     }
     __syncthreads();
     CKV_MARK(chunk, 4);
@@ -1006,258 +725,168 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       float zs = 0.f;
       for (int ch = lane; ch < s.n_chunks; ch += 64) {
         const uint64_t h = L.u.keys[ch * G + j];
-        zs += __uint_as_float((uint32_t)(h >> 32)) * fscale(__uint_as_float((uint32_t)h), mz);
+        zs += __uint_as_float((uint32_t)(h >> 32)) * scale_from(__uint_as_float((uint32_t)h), mz);
       }
       zs = wave_sum_dpp(zs);
-      if (lane == 0) L.lnz[j] = zs > 0.f ? mz + flog(zs) : -INFINITY;
+      if (lane == 0) L.lnz[j] = zs > 0.f ? mz + logf(zs) : -INFINITY;
     }
     __syncthreads();
-    CKV_MARK(chunk, 10);
-    // ranked key of block tid of the chunk (nrows <= NT), and the samples' scores
+    // ranked score of block tid of the chunk (nrows <= NT)
     uint64_t mykey = 0;
-    if (tid < nrows) mykey = fused_key(ranked_score<G>(&L.lam[0][tid], kChunk, L.lnz), start + tid, L.pgt[tid]);
-    const bool real_smp = sampled && tid < NW * QP && tid % QP < s.n_chunks;  // NW * QP <= NT
-    if (sampled && tid < NW * QP)
-      sms[tid] = real_smp ? ranked_score<G>(sml + ((tid / QP) * s.n_chunks + tid % QP) * G, 1, L.lnz) : 0.f;
-    __syncthreads();
-    CKV_MARK(chunk, 12);
-    // The lower bound: the k-th largest sample score.  Each wave counts, for
-    // the samples in its lanes' slots, the samples of its row of QP that
-    // score higher; the four counts are summed, and the smallest score with
-    // fewer than k higher ones is the k-th largest (the score bits of
-    // non-negative floats order like the scores; the zero pads are above
-    // none and are not ranked).
-    if (sampled) {
-      int* rkb = reinterpret_cast<int*>(sms + NW * QP);  // [NW][NT] partial counts
-      uint32_t si[4];
+    if (tid < nrows) {
+      float S = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane + 64 * u;
-        si[u] = e < NW * QP && e % QP < s.n_chunks ? __float_as_uint(sms[e]) : ~0u;
+      for (int j = 0; j < G; ++j) {
+        const float lam = L.lam[j][tid], lz = L.lnz[j];
+        if (lam != -INFINITY && lz != -INFINITY) S += expf(lam - lz);
       }
-      int cnt[4] = {0, 0, 0, 0};
-      CKV_MARK(chunk, 22);
-      if (NW * QP <= 128) count_above<2>(sms + wave * QP, QP, si, cnt);
-      else count_above<4>(sms + wave * QP, QP, si, cnt);
-      CKV_MARK(chunk, 23);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rkb[wave * NT + lane + 64 * u] = cnt[u];
-      if (tid == 0) L.tlo32 = ns >= kk ? ~0u : 0u;
-      __syncthreads();
-      CKV_MARK(chunk, 24);
-      uint32_t lo = ~0u;
-      if (real_smp && ns >= kk) {
-        const int r = rkb[tid] + rkb[NT + tid] + rkb[2 * NT + tid] + rkb[3 * NT + tid];
-        if (r < kk) lo = __float_as_uint(sms[tid]);
-      }
-      lo = wave_reduce(lo, OpUmin{});  // one shared-memory atomic per wave
-      if (lane == 0 && lo != ~0u) atomicMin(&L.tlo32, lo);
+      mykey = fused_key(S, start + tid, L.pgt[tid]);
     }
-    __syncthreads();
-    CKV_MARK(chunk, 13);
-    // this chunk's survivors (keys at or above the bound), in row order
-    const bool surv = sampled && tid < nrows && (uint32_t)(mykey >> 32) >= L.tlo32;
-    const uint64_t sball = __ballot(surv);
-    if (lane == 0) L.wsum[wave] = (uint32_t)__popcll(sball);
-    __syncthreads();
-    int spos = __popcll(sball & ((1ull << lane) - 1ull));
-    int n_s = 0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      spos += v < wave ? (int)L.wsum[v] : 0;
-      n_s += (int)L.wsum[v];
-    }
-    // decode append: the new token's rows are in L2 before any candidate is
-    // published
+    // decode append: the new token's rows are in L2 before any candidate
+    // that leads another workgroup to them is published
     if constexpr (kApp) {
       if (app) __builtin_amdgcn_s_waitcnt(0);
     }
+    // the chunk's top-k candidates, published largest first
     const Coh cand(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8,
                    s.n_xcd > 0);
-    const bool pf = sampled && n_s <= kk;  // the survivors are this chunk's candidates
-    if (pf) {
-      if (surv) {
-        cand.put_u64(chunk * s.kmax + spos, mykey);
-        if (spos < RS) L.srow[spos] = tid;
+    const int k1 = min(kk, nrows);
+    const bool fast = kk <= 64;  // selections of up to one wave's width stay in registers
+    if (fast) {
+      // each wave sorts its 64 blocks; wave 0 merges the four lists
+      const uint64_t srt = wave_sort_desc(mykey);
+      L.u.keys[tid] = srt;
+      __syncthreads();
+      if (wave == 0) {
+        uint64_t top = srt;
+        for (int v = 1; v < NW; ++v) top = wave_merge_desc(top, L.u.keys[64 * v + 63 - lane]);
+        if (lane < kk) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
       }
-      if (tid >= n_s && tid < kk) cand.put_u64(chunk * s.kmax + tid, 1u);  // 1: below every real key
-      n_pf = min(n_s, NPB);
-      n_pv = min(n_s, RS);
     } else {
-      // the chunk's top-k candidates by a radix selection, in row order (the
-      // order is the same in every call: the shared-out gather follows it)
-      const int k1 = min(kk, nrows);
       if (tid < nrows) L.u.keys[tid] = mykey;
       __syncthreads();
       if (k1 > 0) {
         const uint64_t T1 = k1 == nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
-        const bool top = tid < nrows && mykey >= T1;  // nrows <= NT
-        const uint64_t bt = __ballot(top);
-        if (lane == 0) L.wcnt[wave] = (uint32_t)__popcll(bt);
+        if (tid == 0) L.count = 0u;
         __syncthreads();
-        int pos = (int)__popcll(bt & ((1ull << lane) - 1ull));
-#pragma unroll
-        for (int v = 0; v < NW; ++v) pos += v < wave ? (int)L.wcnt[v] : 0;
-        if (top) cand.put_u64(chunk * s.kmax + pos, mykey);
+        for (int i = tid; i < nrows; i += NT) {
+          const uint64_t key = L.u.keys[i];
+          if (key >= T1) cand.put_u64(chunk * s.kmax + (int)atomicAdd(&L.count, 1u), key);
+        }
       }
       for (int e = k1 + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);  // below every real key
     }
     __syncthreads();
+    // the pair's top-k from every chunk's candidates
     CKV_MARK(chunk, 5);
-    if (n_pv > 0) {
-      // rows of the first survivors (row slot rs, slice c), requested now
-      const KV* kc = static_cast<const KV*>(io.k_cache);
-      const KV* vc = static_cast<const KV*>(io.v_cache);
-#pragma unroll
-      for (int u = 0; u < PF; ++u) {
-        const int pb = (u * RS + rs) / kBlockSize, tok = (u * RS + rs) % kBlockSize;
-        pok[u] = false;
-        if (pb < n_pf) {
-          const int ri = L.srow[pb], pg = L.pgt[ri];
-          pok[u] = pg >= 0 && tok < Lseq - (start + ri) * s.bs;
-          if (pok[u]) {
-            const size_t off = (((size_t)pg * s.Hkv + g) * s.bs + tok) * D + c * 8;
-            raw_load(kc + off, pk[u]);
-            raw_load(vc + off, pv[u]);
+    const int n2 = s.n_chunks * kk;
+    read_published(cand, n2, kk, s.kmax, L.u.keys, err);
+    __syncthreads();
+    CKV_MARK(chunk, 6);
+    if (fast) {
+      // A lower bound of the k-th largest candidate: the k-th largest of the
+      // first m candidates of every chunk (at most 64 keys).  The keys at or
+      // above it hold the top k; when they fit in one wave they are sorted
+      // there, then re-sorted by block index, which gives every block's rank.
+      if (wave == 0) {
+        const int m = min(kk, max(1, 64 / s.n_chunks));
+        const int c = lane / m, e = lane % m;
+        const uint64_t v = c < s.n_chunks ? L.u.keys[c * kk + e] : 0ull;
+        const uint64_t srt = wave_sort_desc(v);
+        const int kth = s.n_chunks * m >= kk ? kk - 1 : 63;  // too few keys: no bound (lane 63 holds 0)
+        const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)srt, kth);
+        const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(srt >> 32), kth);
+        if (lane == 0) {
+          L.tlo = (hi << 32) | lo;
+          L.count = 0u;
+        }
+      }
+      __syncthreads();
+      const uint64_t tlo = L.tlo;
+      for (int e = tid; e < n2; e += NT) {
+        const uint64_t key = L.u.keys[e];
+        if (key >= tlo) {
+          const uint32_t pos = atomicAdd(&L.count, 1u);
+          if (pos < 64) L.surv[pos] = key;
+        }
+      }
+      __syncthreads();
+      const uint32_t nsurv = L.count;
+      if (nsurv <= 64) {
+        listed = true;
+        if (wave == 0) {
+          // lane e < kk holds the pair's e-th largest key; the chunks' workgroups
+          // attend to them round robin in that order
+          const uint64_t top = wave_sort_desc(lane < (int)nsurv ? L.surv[lane] : 0ull);
+          const int ti = fused_key_index(top);
+          const bool real = lane < kk && ti >= 0 && ti < M;
+          if (real && lane % s.n_chunks == chunk) {
+            L.gblk[lane / s.n_chunks] = ti;
+            L.gpg[lane / s.n_chunks] = fused_key_page(top);
+          }
+          const bool mine = real && ti >= start && ti < start + nrows;
+          const uint64_t mb = __ballot(mine);
+          if (mine) L.own[__popcll(mb & ((1ull << lane) - 1ull))] = ti - start;
+          if (lane == 0) L.nown = (uint32_t)__popcll(mb);
+          L.surv[lane] = real ? (uint64_t)ti : ~0ull;  // for the selection output, written last
+        }
+        __syncthreads();
+        n_own = (int)L.nown;
+        n_gather = kk > chunk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
+      }
+    }
+    if (!listed) {
+      const int words = (M + 31) / 32;
+      for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
+      __syncthreads();
+      const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
+      for (int e = tid; e < n2; e += NT) {
+        const uint64_t key = L.u.keys[e];
+        const int idx = fused_key_index(key);
+        if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
+      }
+      __syncthreads();
+      // selected blocks before each bitmap word (words <= 2 NT), into hist
+      {
+        const uint32_t w0 = 2 * tid < words ? L.bitmap[2 * tid] : 0u;
+        const uint32_t w1 = 2 * tid + 1 < words ? L.bitmap[2 * tid + 1] : 0u;
+        const uint32_t c0 = __popc(w0), tot = c0 + __popc(w1);
+        const uint32_t inc = wave_scan_incl(tot);
+        if (lane == 63) L.sh[wave] = inc;
+        __syncthreads();
+        uint32_t off = inc - tot;
+        for (int v = 0; v < wave; ++v) off += L.sh[v];
+        L.hist[2 * tid] = off;
+        L.hist[2 * tid + 1] = off + c0;
+      }
+      // this chunk's selected blocks, ascending (kChunk / 32 bitmap words)
+      if (wave == 0) {
+        const int wd = start / 32 + lane;
+        const uint32_t bits = (lane < kChunk / 32 && wd < words) ? L.bitmap[wd] : 0u;
+        const uint32_t cnt = __popc(bits);
+        const uint32_t inc = wave_scan_incl(cnt);
+        uint32_t pos = inc - cnt;
+        for (uint32_t x = bits; x; x &= x - 1) L.own[pos++] = 32 * lane + __ffs(x) - 1;
+        if (lane == 63) L.count = inc;
+      }
+      __syncthreads();
+      n_own = (int)L.count;
+      // The pair's selected blocks are attended to round robin over its chunks
+      // in ascending order: this workgroup takes ranks chunk, chunk + n_chunks, ...
+      for (int e = tid; e < n2; e += NT) {
+        const uint64_t key = L.u.keys[e];
+        const int idx = fused_key_index(key);
+        if (key >= T && idx >= 0 && idx < M) {
+          const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
+          if (rank % s.n_chunks == chunk) {
+            L.gblk[rank / s.n_chunks] = idx;
+            L.gpg[rank / s.n_chunks] = fused_key_page(key);
           }
         }
       }
-      if (rs < n_pv) raw_load(mv + (size_t)L.srow[rs] * D + c * 8, pnv);  // for the take-back
-    }
-    // the pair's candidates, the real ones gathered into L.surv
-    const int n2 = s.n_chunks * kk;
-    read_candidates(cand, n2, kk, s.kmax, L.u.keys, L.surv, &L.ccount, err);
-    __syncthreads();
-    CKV_MARK(chunk, 6);
-    const uint32_t ncand = L.ccount;
-    uint64_t T;
-    CKV_MARK(chunk, 14);
-    if (kk <= kFastK && ncand <= 64) {
-      // The key of rank k - 1 among the candidates (they differ): lane i of
-      // every wave counts the candidates above candidate i among its quarter
-      // of them, then wave 0 adds the four counts.
-      listed = true;
-      {
-        const uint64_t mine = lane < (int)ncand ? L.surv[lane] : ~0ull;
-        const int j0 = wave * 16;
-        int above = 0;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const uint64_t kj = L.surv[j0 + jj];  // LDS broadcast
-          above += j0 + jj < (int)ncand && kj > mine ? 1 : 0;
-        }
-        L.rk[wave][lane] = above;
-      }
+      n_gather = kk > chunk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
       __syncthreads();
-      if (wave == 0) {
-        const int rank = L.rk[0][lane] + L.rk[1][lane] + L.rk[2][lane] + L.rk[3][lane];
-        if (lane < (int)ncand && rank == kk - 1) L.tsel = L.surv[lane];
-        if (lane == 0 && (int)ncand < kk) {  // cannot happen: the bound leaves at least k keys
-          L.tsel = 2u;
-          st_c(err, kErrSelect);
-        }
-      }
-      __syncthreads();
-      T = L.tsel;
-      CKV_MARK(chunk, 15);
-    } else {
-      T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
-      if (chunk == 0) {
-        // the selection output's bitmap, built now: the keys share memory
-        // with the partial's reduction
-        const int words = (M + 31) / 32;
-        for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
-        __syncthreads();
-        for (int e = tid; e < n2; e += NT) {
-          const uint64_t key = L.u.keys[e];
-          const int idx = fused_key_index(key);
-          if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
-        }
-      }
     }
-    // this chunk's selected blocks (keys >= T), in row order: for the
-    // take-back, those whose mean value was not requested early; for the
-    // gather, those whose rows were not (without samples, the same for every
-    // chunk of the pair, the gather is shared out evenly below instead)
-    const bool spread = !sampled;
-    const bool sel = tid < nrows && mykey >= T;
-    const bool in_pf = sel && pf && spos < n_pf;
-    const bool in_pv = sel && pf && spos < n_pv;
-    const uint64_t bsel = __ballot(sel && !in_pv), bgat = __ballot(sel && !in_pf && !spread), btb = __ballot(in_pv);
-    if (lane == 0) {
-      L.wsum[wave] = (uint32_t)__popcll(bsel);
-      L.wsum2[wave] = (uint32_t)__popcll(bgat);
-      L.wsum3[wave] = (uint32_t)__popcll(btb);
-    }
-    if (tid < NPB) L.ssel[tid] = 0u;
-    if (tid < RS) L.tbk[tid] = 0u;
-    __syncthreads();
-    int opos = __popcll(bsel & ((1ull << lane) - 1ull)), gpos = __popcll(bgat & ((1ull << lane) - 1ull));
-#pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      opos += v < wave ? (int)L.wsum[v] : 0;
-      gpos += v < wave ? (int)L.wsum2[v] : 0;
-      n_own += (int)L.wsum[v];
-      n_gather += (int)L.wsum2[v];
-      n_tb += (int)L.wsum3[v];
-    }
-    if (sel && !in_pv) L.own[opos] = tid;
-    if (in_pf) L.ssel[spos] = 1u;
-    if (in_pv) L.tbk[spos] = 1u;
-    if (sel && !in_pf && !spread) {
-      L.gblk[gpos] = start + tid;
-      L.gpg[gpos] = L.pgt[tid];
-    }
-    if (spread) {
-      // The pair's selected blocks shared out evenly: the p-th of them (in
-      // the order below) to chunk p mod n_chunks.  Each wave takes a range
-      // of the candidate array, two entries per lane in one 16-byte read;
-      // it counts its selected entries, then places them after the earlier
-      // waves'.
-      const int per_w = ((n2 + NW - 1) / NW + 127) & ~127;
-      const int e_lo = min(n2, wave * per_w), e_hi = min(n2, e_lo + per_w);
-      const uint4* k4 = reinterpret_cast<const uint4*>(L.u.keys);  // e_lo even: 16-byte pairs
-      const uint64_t lt = (1ull << lane) - 1ull;
-      int cw = 0;
-      for (int e0 = e_lo; e0 < e_hi; e0 += 128) {
-        const int e = e0 + 2 * lane;
-        const uint4 v = e < e_hi ? k4[e >> 1] : make_uint4(0u, 0u, 0u, 0u);
-        const bool sa = e < e_hi && (((uint64_t)v.y << 32) | v.x) >= T;
-        const bool sb = e + 1 < e_hi && (((uint64_t)v.w << 32) | v.z) >= T;
-        cw += (int)(__popcll(__ballot(sa)) + __popcll(__ballot(sb)));
-      }
-      if (lane == 0) L.wcnt[wave] = (uint32_t)cw;
-      __syncthreads();
-      int p0 = 0;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) p0 += v < wave ? (int)L.wcnt[v] : 0;
-      for (int e0 = e_lo; e0 < e_hi; e0 += 128) {
-        const int e = e0 + 2 * lane;
-        const uint4 v = e < e_hi ? k4[e >> 1] : make_uint4(0u, 0u, 0u, 0u);
-        const uint64_t ka = ((uint64_t)v.y << 32) | v.x, kb = ((uint64_t)v.w << 32) | v.z;
-        const bool sa = e < e_hi && ka >= T, sb = e + 1 < e_hi && kb >= T;
-        const uint64_t ba = __ballot(sa), bb = __ballot(sb);
-        const int pa = p0 + (int)(__popcll(ba & lt) + __popcll(bb & lt)), pb = pa + (sa ? 1 : 0);
-        if (sa && pa % s.n_chunks == chunk && pa < kk) {
-          L.gblk[pa / s.n_chunks] = fused_key_index(ka);
-          L.gpg[pa / s.n_chunks] = fused_key_page(ka);
-        }
-        if (sb && pb % s.n_chunks == chunk && pb < kk) {
-          L.gblk[pb / s.n_chunks] = fused_key_index(kb);
-          L.gpg[pb / s.n_chunks] = fused_key_page(kb);
-        }
-        p0 += (int)(__popcll(ba) + __popcll(bb));
-      }
-      n_gather = chunk < kk ? (kk - 1 - chunk) / s.n_chunks + 1 : 0;
-    }
-    __syncthreads();
-    CKV_MARK(chunk, 7);
-    CKV_NOTE(chunk, 16, (uint64_t)n_own);
-    CKV_NOTE(chunk, 17, (uint64_t)n_gather);
-    CKV_NOTE(chunk, 18, (uint64_t)n_tb);
-    CKV_NOTE(chunk, 19, (uint64_t)n_pv);
-    CKV_NOTE(chunk, 20, (uint64_t)n_pf);
-    CKV_NOTE(chunk, 21, (uint64_t)(pf ? 1 : 0));
   } else if (kk == M) {
     // every block selected: each chunk attends to its own
     n_gather = nrows;
@@ -1269,7 +898,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     __syncthreads();
   }
 
-  // ---- exact attention over this chunk's selected blocks ----
+  CKV_MARK(chunk, 7);
+  // ---- exact attention over this workgroup's share of the selected blocks ----
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -1280,70 +910,25 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   {
     // one batch covers UG tokens per row slot (RS * UG tokens), all its loads
-    // issued together; the same in every instance, since the rounding of the
-    // batched update depends on it
-    constexpr int UG = 2;
+    // issued together
+    constexpr int UG = 4;
     const KV* kc = static_cast<const KV*>(io.k_cache);
     const KV* vc = static_cast<const KV*>(io.v_cache);
-    QSlice<KV, G> qs;
-    qs.set(L.qf, D, c);
+    float qv[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[j][e] = L.qf[j * D + c * 8 + e];
     const int ntok = n_gather * kBlockSize;
     // The value workgroup sums the compensation terms of every block of the
     // chunk; the terms of the chunk's selected blocks are taken back here,
     // before any exact term, in the frame of the chunk max.
-    const bool take_back = comp && n_own + n_tb > 0;
+    const bool take_back = comp && n_own > 0;
     if (take_back) {
 #pragma unroll
       for (int j = 0; j < G; ++j) m[j] = L.mx[j];
     }
-    if (take_back) {
-      // survivor rs, if selected: its mean value is in this thread's registers
-      if (rs < n_pv && L.tbk[rs]) {
-        const int ri = L.srow[rs];
-        float nv[8];
-        raw_float(pnv, nv);
-        if constexpr (kApp) {
-          if (app && ri == ti) {
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) nv[e2] = L.tmv[c * 8 + e2];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float wt = L.wt[j][ri];
-          l[j] -= wt;
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) acc[j][e2] = fmaf(-wt, nv[e2], acc[j][e2]);
-        }
-      }
-      for (int e = rs; e < n_own; e += RS) {
-        const int ri = L.own[e];
-        float nv[8];
-        load8(mv + (size_t)ri * D + c * 8, nv);
-        if constexpr (kApp) {
-          if (app && ri == ti) {
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) nv[e2] = L.tmv[c * 8 + e2];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float wt = L.wt[j][ri];
-          l[j] -= wt;
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) acc[j][e2] = fmaf(-wt, nv[e2], acc[j][e2]);
-        }
-      }
-    }
-    // the requested survivors that were selected
-    if constexpr (PF > 0) {
-      bool use[PF];
-#pragma unroll
-      for (int u = 0; u < PF; ++u) use[u] = pok[u] && L.ssel[(u * RS + rs) / kBlockSize];  // uniform across the row
-      attend_rows<KV, G, LPR, PF>(m, l, acc, qs, pk, pv, use, s.tau);
-    }
-    // the other selected blocks
-    for (int t0 = 0; t0 < ntok; t0 += RS * UG) {
+    for (int t0 = 0; t0 < max(ntok, take_back ? 1 : 0); t0 += RS * UG) {
       Raw8<KV> kr[UG], vr[UG];
       bool ok[UG];
 #pragma unroll
@@ -1358,15 +943,47 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           raw_load(vc + off, vr[u]);
         }
       }
-      attend_rows<KV, G, LPR, UG>(m, l, acc, qs, kr, vr, ok, s.tau);  // ok: uniform across the row
+      if (t0 == 0 && take_back) {
+        for (int e = rs; e < n_own; e += RS) {
+          const int ri = L.own[e];
+          float nv[8];
+          load8(mv + (size_t)ri * D + c * 8, nv);
+          if constexpr (kApp) {
+            if (app && ri == ti) {
+#pragma unroll
+              for (int e2 = 0; e2 < 8; ++e2) nv[e2] = L.tmv[c * 8 + e2];
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const float wt = L.wt[j][ri];
+            l[j] -= wt;
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) acc[j][e2] = fmaf(-wt, nv[e2], acc[j][e2]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        if (ok[u]) {  // uniform across the row's lanes
+          float k8[8], v8[8], dot[G];
+          raw_float(kr[u], k8);
+          raw_float(vr[u], v8);
+          dot8<G>(qv, k8, dot);
+#pragma unroll
+          for (int j = 0; j < G; ++j) online_add<G>(m, l, acc, j, group_sum<LPR>(dot[j]) * s.tau, 1.f, v8);
+        }
+      }
     }
   }
+  CKV_MARK(chunk, 8);
   const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + chunk) * G * (D + 2), (size_t)G * (D + 2) * 8,
                  s.n_xcd > 0);
-  CKV_MARK(chunk, 8);
-  // the chunk's value workgroup publishes its compensation sums as a partial
-  // of its own, which the merge reads beside this one
-  publish_partial<D, G>(m, l, acc, L.u.red, part, tag, nullptr, err);
+  // the value workgroup of this chunk publishes its compensation sums first;
+  // they are folded into this partial, so the merge reads one per chunk
+  const Coh vpart(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
+                  (size_t)G * (D + 2) * 8, s.n_xcd > 0);
+  publish_partial<D, G>(m, l, acc, L.u.red, part, tag, &vpart, err);
   CKV_MARK(chunk, 9);
   CKV_NOTE(chunk, 26, __builtin_amdgcn_s_memtime());
 
@@ -1380,19 +997,16 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (!listed) {
           emit_selection<NT>(M, L.bitmap, L.wsum, out, kk, nullptr, 0, 0);
         } else if (wave == 0) {
-          // by ascending block index: a selected block's place is the number
-          // of selected blocks with a lower index
-          const uint32_t ncand = L.ccount;
-          const uint64_t T = L.tsel;
-          const uint64_t mine = lane < (int)ncand ? L.surv[lane] : 0ull;
-          const bool chosen = lane < (int)ncand && mine >= T;
-          const int idx = fused_key_index(mine);
-          int place = 0;
-          for (int j = 0; j < (int)ncand; ++j) {
-            const uint64_t kj = L.surv[j];  // LDS broadcast
-            place += kj >= T && fused_key_index(kj) < idx ? 1 : 0;
-          }
-          if (chosen && place < kk) out[place] = idx;
+          // by ascending block index: a block's place is the number of selected
+          // blocks with a lower index (the indices differ)
+          const uint64_t sv = L.surv[lane];
+          const bool real = lane < kk && sv != ~0ull;
+          const int ti = (int)(uint32_t)sv;
+          const int nreal = __popcll(__ballot(real));  // the real entries come first
+          int rank = 0;
+          for (int e = 0; e < nreal; ++e) rank += (int)(uint32_t)L.surv[e] < ti ? 1 : 0;  // LDS broadcast
+          if (real) out[rank] = ti;
+          else if (lane >= nreal && lane < kk) out[lane] = -1;
         }
       } else
         for (int i = tid; i < kk; i += NT) out[i] = i;
@@ -1404,7 +1018,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 // Value workgroup of chunk `chunk` of pair bg: the compensation terms of every
 // block of the chunk, n e^{s_bar} mean_v, with the control workgroup's weights.
 // ---------------------------------------------------------------------------
-template <typename KV, int D, int G, bool kApp>
+template <typename KV, int D, int G>
 __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
                           ValLds<D, G>& L) {
   constexpr int LPR = D / 8, RS = NT / LPR, RPL = kChunk / RS;
@@ -1420,26 +1034,15 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   const Buf mvb(static_cast<const KV*>(io.summ.mean_v) + ((size_t)bg * s.max_blocks + start) * D,
                 nrows * D * sizeof(KV));
   uint32_t* err = w.ctrl + 2;
-  CKV_MARK(s.n_chunks + chunk, 0);
 
   float m[G], l[G], acc[G][8];
+  CKV_MARK(s.n_chunks + chunk, 0);
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-  }
-  // bf16 with G <= 4: the chunk's mean values are requested on entry, all
-  // at once (RPL 16-byte pieces per thread), and arrive while the control
-  // workgroup scores the mean keys.  Otherwise (more registers, or the
-  // decode append, whose tail row the control workgroup rewrites before it
-  // publishes the weights) they stream below, after the weights.
-  constexpr bool kEarly = sizeof(KV) == 2 && G <= 4 && !kApp;
-  Raw8<KV> nue[kEarly ? RPL : 1];
-  if (kEarly && comp) {
-#pragma unroll
-    for (int jj = 0; jj < RPL; ++jj) raw_load(mvb, (rs + jj * RS) * D + c * 8, nue[jj]);  // 0 past the chunk
   }
   if (comp) {
     const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8, s.n_xcd > 0);
@@ -1458,27 +1061,14 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 #pragma unroll
     for (int j = 0; j < G; ++j) m[j] = L.mx[j];
     CKV_MARK(s.n_chunks + chunk, 1);
-    if constexpr (kEarly) {
-#pragma unroll
-      for (int jj = 0; jj < RPL; ++jj) {
-        const int ri = rs + jj * RS;
-        if (ri < nrows) {
-          float x[8];
-          raw_float(nue[jj], x);
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            const float wt = L.w[j][ri];
-            l[j] += wt;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(wt, x[e], acc[j][e]);
-          }
-        }
-      }
-    }
-    // Otherwise the mean values stream kValRows rows per thread at a time.
+    // The mean values stream kValRows rows per thread at a time.  Their sums
+    // are needed late (when the control workgroup publishes, some 10 us on),
+    // and requesting every row at once floods the memory system while the
+    // control workgroups hand headers and candidates to each other: measured,
+    // 4 rows at a time beat 2, 8 and all 16.
     constexpr int kValRows = RPL < 4 ? RPL : 4;
 #pragma unroll 1
-    for (int g0 = 0; g0 < (kEarly ? 0 : RPL); g0 += kValRows) {
+    for (int g0 = 0; g0 < RPL; g0 += kValRows) {
       Raw8<KV> nu[kValRows];
 #pragma unroll
       for (int jj = 0; jj < kValRows; ++jj) raw_load(mvb, (rs + (g0 + jj) * RS) * D + c * 8, nu[jj]);  // 0 past the chunk
@@ -1509,10 +1099,10 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 
 // ---------------------------------------------------------------------------
 // Control workgroup `slot` of the pair merges its slice of the pair's output
-// from the partials of all the pair's control and value workgroups, waiting
-// for each to carry this call's tag.  The value workgroups take no part:
-// once their sums are published they leave, instead of polling beside the
-// control workgroups on the same CUs.
+// from the partials of all the pair's control workgroups (each holding its
+// chunk's compensation sums too), waiting for each to carry this call's tag.
+// The value workgroups take no part: once their sums are published they
+// leave, instead of polling beside the control workgroups on the same CUs.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int bg, int slot, uint32_t epoch,
@@ -1523,8 +1113,8 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t tag = epoch + 1u;
   uint32_t* err = w.ctrl + 2;
-  const int nm = s.n_chunks;      // merging workgroups of the pair
-  const int np = 2 * s.n_chunks;  // partials: the control and the value workgroup of each chunk
+  const int nm = s.n_chunks;  // merging workgroups of the pair
+  const int np = s.n_chunks;  // partials: one per chunk (value sums folded in)
   const int per = (NV + nm - 1) / nm;  // float4 outputs of this workgroup
   const int step = max(1, NT / np);    // outputs merged per pass
   const int o0 = slot * per, o1 = min(NV, o0 + per);
@@ -1563,7 +1153,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
       float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int p = lane; p < np; p += 64) {
         const int it = oo * np + p;
-        const float f = fscale(L.pm[it], Mx);
+        const float f = scale_from(L.pm[it], Mx);
         Ls = fmaf(L.pl[it], f, Ls);
         A.x = fmaf(L.pa[it].x, f, A.x);
         A.y = fmaf(L.pa[it].y, f, A.y);
@@ -1582,7 +1172,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
         op[1] = Ls > 0.f ? A.y / Ls : 0.f;
         op[2] = Ls > 0.f ? A.z / Ls : 0.f;
         op[3] = Ls > 0.f ? A.w / Ls : 0.f;
-        if (d4 == 0 && io.lse) io.lse[(size_t)b * s.Hq + h] = Ls > 0.f ? Mx + flog(Ls) : -INFINITY;
+        if (d4 == 0 && io.lse) io.lse[(size_t)b * s.Hq + h] = Ls > 0.f ? Mx + logf(Ls) : -INFINITY;
       }
     }
     __syncthreads();
@@ -1649,9 +1239,6 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s_arg, StepIO i
   for (int bg = pair; bg < s.B * s.Hkv; bg += s.bg_round) {
     const uint32_t epoch = ld_uniform(ctr_epoch(w, bg));  // advanced by the previous call
     if (role < s.n_chunks) {
-      // A control workgroup shares its CU with a value workgroup, whose sums
-      // are needed only at the merge: the control waves issue first.
-      __builtin_amdgcn_s_setprio(3);
       ctl_chunk<KV, D, G, kR4, kApp>(s, io, w, bg, role, epoch + 1u, lds.c);
       __syncthreads();
       merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m);
@@ -1659,7 +1246,7 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s_arg, StepIO i
     } else {
       // value workgroup v sums chunks v, v + n_val, ... in turn
       for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
-        val_chunk<KV, D, G, kApp>(s, io, w, bg, chunk, epoch + 1u, lds.v);
+        val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
         __syncthreads();
       }
       // then clear its chunks' rows of the previous call's headers and

@@ -8,7 +8,7 @@ rotating layer buffers) with libcompkv_trace.so, the library built with
 CKV_PHASE_TRACE.  In that build, thread 0 of every workgroup of the single
 launch stores the 100 MHz constant-rate clock (s_memrealtime) at fixed points
 of its work into the workspace's per-block score region, which the single
-launch leaves unused, together with a few counts.  This reads the marks left
+launch leaves unused.  This reads the marks left
 by the last step and prints, per phase, the median and the maximum over the
 workgroups, in microseconds from the first workgroup's entry.  The trace
 build stores a handful of words per workgroup, so its step takes about as
@@ -29,14 +29,10 @@ from . import workloads as W
 from .tensors import to_device
 
 MARKS_PER_SLOT = 32
-CONTROL = {0: "entry", 1: "q staged", 2: "mean keys scored", 3: "header, weights, samples published",
-           4: "headers and samples read", 10: "log Z_hat", 12: "keys and sample scores",
-           13: "lower bound", 5: "candidates published", 6: "candidates read",
-           15: "T by ranks (one-wave list)", 7: "selection known", 8: "exact attention done",
-           9: "partial published", 11: "merged (output written)"}
+CONTROL = {0: "entry", 1: "q staged", 2: "mean keys scored", 3: "header and weights published",
+           4: "headers read", 5: "candidates published", 6: "candidates read", 7: "selection known",
+           8: "exact attention done", 9: "partial published", 11: "merged (output written)"}
 VALUE = {0: "entry", 1: "weights read", 2: "mean values summed", 3: "partial published"}
-COUNTS = ("own take-back", "gathered", "taken back from registers", "mean values requested early",
-          "rows requested early", "survivors were the candidates")
 
 
 def main(argv=None) -> int:
@@ -114,8 +110,6 @@ def main(argv=None) -> int:
     ok = (span > 0) & (cyc > 0)
     if ok.any():
         print(f"shader clock over entry .. partial published: {np.median(cyc[ok] / span[ok] * 100.0):.0f} MHz")
-    counts = words[:, :nch, 16:22].reshape(-1, 6)
-    print("mean per control workgroup: " + ", ".join(f"{n} {m:.2f}" for n, m in zip(COUNTS, counts.mean(axis=0))))
     return 0
 
 
