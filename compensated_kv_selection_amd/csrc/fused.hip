@@ -238,7 +238,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
     uint32_t mb = __float_as_uint(m[j]);
     if (LPR == 8) mb = OpFmax{}(mb, dpp_row_ror8(mb));
     const float mw = __uint_as_float(across_rows(mb, OpFmax{}));
-    const float f = scale_from(m[j], mw);
+    const float f = fscale(m[j], mw);
     uint32_t lb = __float_as_uint(l[j] * f);
     if (LPR == 8) lb = OpFadd{}(lb, dpp_row_ror8(lb));
     const float lw = __uint_as_float(across_rows(lb, OpFadd{}));
@@ -269,7 +269,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
       const float* rw = red[v][j];
-      const float f = scale_from(rw[0], Mx);
+      const float f = fscale(rw[0], Mx);
       a0 = fmaf(rw[4 + 2 * d2], f, a0);
       a1 = fmaf(rw[4 + 2 * d2 + 1], f, a1);
       Ls = fmaf(rw[1], f, Ls);
@@ -284,7 +284,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
       const float le = read_tagged(*extra, h + 1, w1, tag, spins, err);
       const float e0 = read_tagged(*extra, h + 2 + 2 * d2, w2, tag, spins, err);
       const float e1 = read_tagged(*extra, h + 3 + 2 * d2, w3, tag, spins, err);
-      const float M = fmaxf(Mx, me), f1 = scale_from(Mx, M), f2 = scale_from(me, M);
+      const float M = fmaxf(Mx, me), f1 = fscale(Mx, M), f2 = fscale(me, M);
       a0 = a0 * f1 + e0 * f2;
       a1 = a1 * f1 + e1 * f2;
       Ls = Ls * f1 + le * f2;
@@ -295,6 +295,94 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
     if (d2 == 0) {
       part.put_u64(h, tagged(Mx, tag));
       part.put_u64(h + 1, tagged(Ls, tag));
+    }
+  }
+}
+
+// This thread's 8-channel slice of the G query rows, as the dot products
+// with a key slice want it: bf16 pairs for bf16 keys (multiplied exactly,
+// summed in fp32 by v_dot2), fp32 otherwise.
+template <typename KV, int G> struct QSlice;
+template <int G> struct QSlice<uint16_t, G> {
+  uint32_t p[G][4];
+  __device__ __forceinline__ void set(const float* qf, int D, int c) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)  // the floats hold bf16 values: their upper halves are the bf16 bits
+        p[j][e] = (__float_as_uint(qf[j * D + c * 8 + 2 * e]) >> 16) |
+                  (__float_as_uint(qf[j * D + c * 8 + 2 * e + 1]) & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ void dot(const Raw8<uint16_t>& k, float (&d)[G]) const {
+    const uint32_t kw[4] = {k.a.x, k.a.y, k.a.z, k.a.w};
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw[e]), __builtin_bit_cast(bf16x2_t, p[j][e]),
+                                            a, false);
+      d[j] = a;
+    }
+  }
+};
+template <int G> struct QSlice<float, G> {
+  float q[G][8];
+  __device__ __forceinline__ void set(const float* qf, int D, int c) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[j][e] = qf[j * D + c * 8 + e];
+  }
+  __device__ __forceinline__ void dot(const Raw8<float>& k, float (&d)[G]) const {
+    float x[8];
+    raw_float(k, x);
+    dot8<G>(q, x, d);
+  }
+};
+
+// Exact attention to up to N token rows (row slot u in use on every lane of
+// its row, or on none): the logits of all of them first, then one online
+// update per head, so that the state's max moves once per batch.
+template <typename KV, int G, int LPR, int N>
+__device__ __forceinline__ void attend_rows(float (&m)[G], float (&l)[G], float (&acc)[G][8], const QSlice<KV, G>& q,
+                                            const Raw8<KV> (&kr)[N], const Raw8<KV> (&vr)[N], const bool (&use)[N],
+                                            float tau) {
+  float x[N][G], mn[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) mn[j] = m[j];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    if (use[u]) {
+      float d[G];
+      q.dot(kr[u], d);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        x[u][j] = token_row_sum<LPR>(d[j]) * tau;
+        mn[j] = fmaxf(mn[j], x[u][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float sc = fscale(m[j], mn[j]);
+    l[j] *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] *= sc;
+    m[j] = mn[j];
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    if (use[u]) {
+      float v8[8];
+      raw_float(vr[u], v8);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float p = fexp(x[u][j] - m[j]);
+        l[j] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p, v8[e], acc[j][e]);
+      }
     }
   }
 }
@@ -683,10 +771,10 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         const int n = min(s.bs, Lseq - (start + ri) * s.bs);
         const float sb = L.sb[j][ri], half = 0.5f * L.lam[j][ri];
         const float massf = (float)n * (1.f + half);  // second-order mass estimate / e^{s_bar}
-        const float wt = (float)n * expf(sb - mx);
+        const float wt = (float)n * fexp(sb - mx);
         z = fmaf(wt, 1.f + half, z);
         L.wt[j][ri] = wt;
-        L.lam[j][ri] = io.score_mode == kScoreMass ? sb + logf(massf) : sb + logf(massf * half);
+        L.lam[j][ri] = io.score_mode == kScoreMass ? sb + flog(massf) : sb + flog(massf * half);
         if (comp) wts.put_u64(j * kWStride + ri, tagged(wt, tag));
       }
       z = wave_sum_dpp(z);
@@ -725,10 +813,10 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       float zs = 0.f;
       for (int ch = lane; ch < s.n_chunks; ch += 64) {
         const uint64_t h = L.u.keys[ch * G + j];
-        zs += __uint_as_float((uint32_t)(h >> 32)) * scale_from(__uint_as_float((uint32_t)h), mz);
+        zs += __uint_as_float((uint32_t)(h >> 32)) * fscale(__uint_as_float((uint32_t)h), mz);
       }
       zs = wave_sum_dpp(zs);
-      if (lane == 0) L.lnz[j] = zs > 0.f ? mz + logf(zs) : -INFINITY;
+      if (lane == 0) L.lnz[j] = zs > 0.f ? mz + flog(zs) : -INFINITY;
     }
     __syncthreads();
     // ranked score of block tid of the chunk (nrows <= NT)
@@ -738,7 +826,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float lam = L.lam[j][tid], lz = L.lnz[j];
-        if (lam != -INFINITY && lz != -INFINITY) S += expf(lam - lz);
+        if (lam != -INFINITY && lz != -INFINITY) S += fexp(lam - lz);
       }
       mykey = fused_key(S, start + tid, L.pgt[tid]);
     }
@@ -910,15 +998,13 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   {
     // one batch covers UG tokens per row slot (RS * UG tokens), all its loads
-    // issued together
+    // issued together; the same in every instance, since the rounding of the
+    // batched update depends on it
     constexpr int UG = 4;
     const KV* kc = static_cast<const KV*>(io.k_cache);
     const KV* vc = static_cast<const KV*>(io.v_cache);
-    float qv[G][8];
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[j][e] = L.qf[j * D + c * 8 + e];
+    QSlice<KV, G> qs;
+    qs.set(L.qf, D, c);
     const int ntok = n_gather * kBlockSize;
     // The value workgroup sums the compensation terms of every block of the
     // chunk; the terms of the chunk's selected blocks are taken back here,
@@ -963,17 +1049,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           }
         }
       }
-#pragma unroll
-      for (int u = 0; u < UG; ++u) {
-        if (ok[u]) {  // uniform across the row's lanes
-          float k8[8], v8[8], dot[G];
-          raw_float(kr[u], k8);
-          raw_float(vr[u], v8);
-          dot8<G>(qv, k8, dot);
-#pragma unroll
-          for (int j = 0; j < G; ++j) online_add<G>(m, l, acc, j, group_sum<LPR>(dot[j]) * s.tau, 1.f, v8);
-        }
-      }
+      attend_rows<KV, G, LPR, UG>(m, l, acc, qs, kr, vr, ok, s.tau);  // ok: uniform across the row
     }
   }
   CKV_MARK(chunk, 8);
@@ -1153,7 +1229,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
       float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int p = lane; p < np; p += 64) {
         const int it = oo * np + p;
-        const float f = scale_from(L.pm[it], Mx);
+        const float f = fscale(L.pm[it], Mx);
         Ls = fmaf(L.pl[it], f, Ls);
         A.x = fmaf(L.pa[it].x, f, A.x);
         A.y = fmaf(L.pa[it].y, f, A.y);
@@ -1172,7 +1248,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
         op[1] = Ls > 0.f ? A.y / Ls : 0.f;
         op[2] = Ls > 0.f ? A.z / Ls : 0.f;
         op[3] = Ls > 0.f ? A.w / Ls : 0.f;
-        if (d4 == 0 && io.lse) io.lse[(size_t)b * s.Hq + h] = Ls > 0.f ? Mx + logf(Ls) : -INFINITY;
+        if (d4 == 0 && io.lse) io.lse[(size_t)b * s.Hq + h] = Ls > 0.f ? Mx + flog(Ls) : -INFINITY;
       }
     }
     __syncthreads();

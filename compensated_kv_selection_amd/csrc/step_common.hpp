@@ -27,6 +27,8 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 // to zero.
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 __device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+// exp(a - m), 0 for an empty state (a = -inf)
+__device__ __forceinline__ float fscale(float a, float m) { return a == -INFINITY ? 0.f : fexp(a - m); }
 
 // ---- coherent access to workspace written inside the same launch -----------
 // The XCDs of the device have separate L2 caches.  Words that one workgroup
