@@ -102,7 +102,7 @@ ckv_status make_shape(const ckv_dims* d, int32_t budget_tokens, ckv::Shape* s) {
 }
 
 struct Layout {
-  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, fw, fpart, fsmp, total;
+  size_t ctrl, xs, cpart, cand, gpart, fhdr, fcand, fw, fpart, total;
 };
 
 size_t ctrl_bytes(const ckv::Shape& s) {
@@ -112,7 +112,7 @@ size_t ctrl_bytes(const ckv::Shape& s) {
 // Sparse-step workspace: control words, per-block scores, chunk partials,
 // first-level select candidates, gather partials, and what the fused step
 // hands between workgroups: chunk headers and candidates (zero between
-// calls), tagged compensation weights, chunk partials and chunk samples.
+// calls), tagged compensation weights and chunk partials.
 Layout layout(const ckv::Shape& s) {
   Layout L;
   const size_t pst = ckv::kPartStride(s.D);
@@ -137,8 +137,6 @@ Layout layout(const ckv::Shape& s) {
   off += align_up(bg * s.n_chunks * s.G * (ckv::kChunk + 1) * sizeof(uint64_t));
   L.fpart = off;
   off += align_up(bg * 2 * s.n_chunks * s.G * (size_t)(s.D + 2) * sizeof(uint64_t));
-  L.fsmp = off;
-  off += align_up(bg * s.n_chunks * 4 * s.G * sizeof(uint64_t));
   L.total = off;
   return L;
 }
@@ -150,7 +148,7 @@ ckv::Work carve(const ckv::Shape& s, void* ws) {
                    reinterpret_cast<float*>(base + L.cpart), reinterpret_cast<uint64_t*>(base + L.cand),
                    reinterpret_cast<float*>(base + L.gpart), reinterpret_cast<uint64_t*>(base + L.fhdr),
                    reinterpret_cast<uint64_t*>(base + L.fcand), reinterpret_cast<uint64_t*>(base + L.fw),
-                   reinterpret_cast<uint64_t*>(base + L.fpart), reinterpret_cast<uint64_t*>(base + L.fsmp)};
+                   reinterpret_cast<uint64_t*>(base + L.fpart)};
 }
 
 // Dense splits: about 256 workgroups in all (one per CU), a
@@ -570,7 +568,7 @@ ckv_status ckv_dense_decode_attention(const ckv_dims* dims, const void* q, const
     return fail(CKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(workspace);
   ckv::Work w{reinterpret_cast<uint32_t*>(base), nullptr, nullptr, nullptr,
-              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr, nullptr, nullptr, nullptr};
+              reinterpret_cast<float*>(base + ctrl_bytes(s)), nullptr, nullptr, nullptr, nullptr};
   ckv::StepIO io{q, k_cache, v_cache, ckv::Summ{nullptr, nullptr, nullptr, nullptr}, block_table,
                  seq_lens, nullptr, nullptr, nullptr, out, lse, 0, 0};
   return hip_status(ckv::launch_step(s, ckv::kModeDense, io, w, static_cast<hipStream_t>(stream)),

@@ -78,8 +78,6 @@ struct Work {
                    //   max, tagged
   uint64_t* fpart; // [B][Hkv][2 * n_chunks][G][D+2] fused: control and value partials
                    //   (max, sum, acc[D]), tagged
-  uint64_t* fsmp;  // [B][Hkv][n_chunks][4][G] fused: per chunk, four sample blocks' per-head
-                   //   log-scores, tagged
 };
 
 struct Summ {

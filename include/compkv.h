@@ -285,7 +285,7 @@ ckv_status ckv_workspace_status(void* workspace, size_t workspace_bytes, uint32_
  * is no workspace argument: the step runs in a workspace built into the
  * library, CKV_NOALLOC_WORKSPACE_BYTES on each device, which covers, for
  * example, 16 sequences of 64K tokens with 8 KV heads, d = 128 and a budget
- * of 1024 tokens (55 MiB).  The call allocates nothing.
+ * of 1024 tokens (49 MiB).  The call allocates nothing.
  *   CKV_ERR_WORKSPACE: ckv_workspace_bytes(dims, budget_tokens) is larger
  *     than CKV_NOALLOC_WORKSPACE_BYTES (checked before anything is enqueued).
  *   CKV_ERR_UNSUPPORTED: the current device's ordinal is 64 or more.

@@ -7,7 +7,7 @@ def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
     """Region sizes of the sparse-step workspace, each 256-byte aligned:
     control words, per-block scores, chunk partials, select candidates,
     gather partials, fused chunk headers, fused candidates, fused tagged
-    weights, fused partials, fused chunk samples."""
+    weights, fused partials."""
     def up(x):
         return (x + 255) // 256 * 256
     G = Hq // Hkv
@@ -20,8 +20,7 @@ def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
     return [up((64 + 8 * bg) * 4), up(B * Hq * max_blocks * 4), up(bg * n_chunks * G * pst * 4),
             up(bg * n_slices * kcap * 8), up(bg * n_splits * G * 2 * pst * 4),
             up(2 * bg * n_chunks * G * 8), up(2 * bg * n_chunks * kcap * 8),
-            up(bg * n_chunks * G * 257 * 8), up(bg * 2 * n_chunks * G * (D + 2) * 8),
-            up(bg * n_chunks * 4 * G * 8)]
+            up(bg * n_chunks * G * 257 * 8), up(bg * 2 * n_chunks * G * (D + 2) * 8)]
 
 
 # Fused chunk headers ([2][B*Hkv][n_chunks][G] words) and candidates
