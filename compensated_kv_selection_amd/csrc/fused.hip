@@ -927,7 +927,9 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       const int words = (M + 31) / 32;
       for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
       __syncthreads();
+      CKV_MARK(chunk, 12);
       const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
+      CKV_MARK(chunk, 13);
       for (int e = tid; e < n2; e += NT) {
         const uint64_t key = L.u.keys[e];
         const int idx = fused_key_index(key);
@@ -947,6 +949,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         L.hist[2 * tid] = off;
         L.hist[2 * tid + 1] = off + c0;
       }
+      CKV_MARK(chunk, 14);
       // this chunk's selected blocks, ascending (kChunk / 32 bitmap words)
       if (wave == 0) {
         const int wd = start / 32 + lane;

@@ -30,7 +30,9 @@ from .tensors import to_device
 
 MARKS_PER_SLOT = 32
 CONTROL = {0: "entry", 1: "q staged", 2: "mean keys scored", 3: "header and weights published",
-           4: "headers read", 5: "candidates published", 6: "candidates read", 7: "selection known",
+           4: "headers read", 5: "candidates published", 6: "candidates read",
+           12: "radix select: start", 13: "radix select: T known", 14: "selected blocks counted",
+           7: "selection known",
            8: "exact attention done", 9: "partial published", 11: "merged (output written)"}
 VALUE = {0: "entry", 1: "weights read", 2: "mean values summed", 3: "partial published"}
 
