@@ -242,12 +242,6 @@ __device__ void scan_role(const Shape& s, const StepIO& io, const Work& w, int t
                                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-#pragma unroll
-  for (int jj = 0; jj < RPL; ++jj) {
-    const int ri = rs + jj * RS;
-    if (ri < nrows) raw_load(mv + (size_t)ri * D + c * 8, nu[jj]);
-    else raw_zero(nu[jj]);
-  }
   if (qld) {
     float x[8];
     raw_float(qraw, x);
@@ -327,6 +321,15 @@ __device__ void scan_role(const Shape& s, const StepIO& io, const Work& w, int t
     }
   }
   __syncthreads();
+  // pass B's mean values, requested once pass A has consumed the mean keys:
+  // holding both in registers from entry would halve the workgroups a CU can
+  // hold; their round trip overlaps the log-scores below
+#pragma unroll
+  for (int jj = 0; jj < RPL; ++jj) {
+    const int ri = rs + jj * RS;
+    if (ri < nrows) raw_load(mv + (size_t)ri * D + c * 8, nu[jj]);
+    else raw_zero(nu[jj]);
+  }
 
   // ---- log-scores, chunk maxima, compensation weights, Z_hat partial ----
   float* part = w.cpart + ((size_t)bg * s.n_chunks + chunk) * G * PST;
@@ -1055,8 +1058,12 @@ __global__ __launch_bounds__(kThreads, 2) void dense_kernel(Shape s, StepIO io, 
 // ---------------------------------------------------------------------------
 // The step kernel.  blockIdx.x: [scans], [slices] or [gathers], by mode.
 // ---------------------------------------------------------------------------
+// The bf16 scan is a streaming pass over every chunk: it is held to 128
+// registers so that four workgroups share a CU; the other roles keep what
+// they need.
 template <typename KV, int D, int G, int MODE>
-__global__ __launch_bounds__(kThreads) void step_kernel(Shape s, StepIO io, Work w) {
+__global__ __launch_bounds__(kThreads, MODE == kModeScanOnly && sizeof(KV) == 2 && G <= 4 ? 4 : 1) void step_kernel(
+    Shape s, StepIO io, Work w) {
   __shared__ StepLds<D, G> lds;
   __shared__ int blk[kShareMax];
   __shared__ uint32_t slot;
