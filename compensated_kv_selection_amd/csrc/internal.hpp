@@ -13,8 +13,8 @@ constexpr int kChunk = 256;         // blocks scored by one scan workgroup
 constexpr int kSlice = 1024;        // blocks ranked by one select workgroup
 constexpr int kGatherPages = 4;     // selected blocks per gather workgroup (unfused path)
 constexpr int kMaxSplits = 64;      // gather workgroups per (sequence, KV head), unfused path
-constexpr int kGatherGroups = 512;  // gather workgroups of one attend launch at most (two per CU of
-                                    //   MI355X): more would run in rounds of dependent loads
+constexpr int kGatherGroups = 256;  // gather workgroups of one attend launch at most, one per CU of
+                                    //   MI355X (measured: 256 beat 128, 512 and 1024 on 128 pairs)
 constexpr int kDensePages = 128;    // blocks per dense workgroup
 constexpr int kMaxBlocks = 15872;   // blocks per sequence (page-table width)
 constexpr int kMaxKvHeads = 64;

@@ -16,7 +16,7 @@ def workspace_regions(B, Hq, Hkv, D, max_blocks, budget):
     n_chunks, n_slices = -(-max_blocks // 256), -(-max_blocks // 1024)
     kmax = min(max_blocks, budget // 16)
     kcap = max(kmax, 1)
-    n_splits = min(64, max(1, min((kmax + 3) // 4, max(1, 512 // bg)), -(-kmax // 256)))
+    n_splits = min(64, max(1, min((kmax + 3) // 4, max(1, 256 // bg)), -(-kmax // 256)))
     return [up((64 + 8 * bg) * 4), up(B * Hq * max_blocks * 4), up(bg * n_chunks * G * pst * 4),
             up(bg * n_slices * kcap * 8), up(bg * n_splits * G * 2 * pst * 4),
             up(2 * bg * n_chunks * G * 8), up(2 * bg * n_chunks * kcap * 8),
