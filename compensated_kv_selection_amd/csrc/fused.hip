@@ -930,10 +930,15 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       CKV_MARK(chunk, 12);
       const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
       CKV_MARK(chunk, 13);
-      for (int e = tid; e < n2; e += NT) {
-        const uint64_t key = L.u.keys[e];
-        const int idx = fused_key_index(key);
-        if (key >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
+      for (int e0 = tid; e0 < n2; e0 += 4 * NT) {  // four keys requested at a time
+        uint64_t kb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kb[u] = e0 + u * NT < n2 ? L.u.keys[e0 + u * NT] : 0ull;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = fused_key_index(kb[u]);
+          if (e0 + u * NT < n2 && kb[u] >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
+        }
       }
       __syncthreads();
       // selected blocks before each bitmap word (words <= 2 NT), into hist
@@ -964,14 +969,20 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       n_own = (int)L.count;
       // The pair's selected blocks are attended to round robin over its chunks
       // in ascending order: this workgroup takes ranks chunk, chunk + n_chunks, ...
-      for (int e = tid; e < n2; e += NT) {
-        const uint64_t key = L.u.keys[e];
-        const int idx = fused_key_index(key);
-        if (key >= T && idx >= 0 && idx < M) {
-          const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
-          if (rank % s.n_chunks == chunk) {
-            L.gblk[rank / s.n_chunks] = idx;
-            L.gpg[rank / s.n_chunks] = fused_key_page(key);
+      for (int e0 = tid; e0 < n2; e0 += 4 * NT) {  // four keys requested at a time
+        uint64_t kb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kb[u] = e0 + u * NT < n2 ? L.u.keys[e0 + u * NT] : 0ull;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint64_t key = kb[u];
+          const int idx = fused_key_index(key);
+          if (e0 + u * NT < n2 && key >= T && idx >= 0 && idx < M) {
+            const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
+            if (rank % s.n_chunks == chunk) {
+              L.gblk[rank / s.n_chunks] = idx;
+              L.gpg[rank / s.n_chunks] = fused_key_page(key);
+            }
           }
         }
       }

@@ -287,11 +287,21 @@ __device__ uint64_t radix_kth_largest(const KeyAt key_at, int n, int k, uint32_t
   constexpr int NW = NT / 64;
   static_assert(NW <= 12, "scratch words");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // keys are read four per thread at a time, all requested before the first
+  // is used (one round trip per four instead of per key)
+  constexpr int KB = 4;
   uint64_t kor = 0, kand = ~0ull;
-  for (int i = tid; i < n; i += NT) {
-    const uint64_t key = key_at(i);
-    kor |= key;
-    kand &= key;
+  for (int i0 = tid; i0 < n; i0 += KB * NT) {
+    uint64_t kb[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) kb[u] = i0 + u * NT < n ? key_at(i0 + u * NT) : 0ull;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (i0 + u * NT < n) {
+        kor |= kb[u];
+        kand &= kb[u];
+      }
+    }
   }
   const uint32_t ohi = wave_reduce((uint32_t)(kor >> 32), OpOr{}), olo = wave_reduce((uint32_t)kor, OpOr{});
   const uint32_t ahi = wave_reduce((uint32_t)(kand >> 32), OpAnd{}), alo = wave_reduce((uint32_t)kand, OpAnd{});
@@ -323,11 +333,16 @@ __device__ uint64_t radix_kth_largest(const KeyAt key_at, int n, int k, uint32_t
     uint32_t* h = hist + 256 * (pass & 1);
     uint32_t* h_next = hist + 256 * ((pass + 1) & 1);
     for (int e = tid; e < 256; e += NT) h_next[e] = 0u;
-    for (int i = tid; i < n; i += NT) {
-      const uint64_t key = key_at(i);
-      if ((key & pmask) == prefix) {
-        const uint32_t d = (uint32_t)((lo >= 0 ? key >> lo : key << -lo) & 255u);
-        atomicAdd(&h[d], 1u);
+    for (int i0 = tid; i0 < n; i0 += KB * NT) {
+      uint64_t kb[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) kb[u] = i0 + u * NT < n ? key_at(i0 + u * NT) : 0ull;
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if (i0 + u * NT < n && (kb[u] & pmask) == prefix) {
+          const uint32_t d = (uint32_t)((lo >= 0 ? kb[u] >> lo : kb[u] << -lo) & 255u);
+          atomicAdd(&h[d], 1u);
+        }
       }
     }
     __syncthreads();
