@@ -83,6 +83,7 @@ constexpr int NW = NT / 64;                // waves per workgroup
 #define CKV_MARK(slot, i) CKV_NOTE(slot, i, 0)
 #endif
 
+constexpr int kTier1 = 32;  // k > 64: each chunk's candidates read first (plus the next key)
 constexpr int kPollBatch = 8;              // published words read per thread per round trip
 constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
 constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
@@ -114,6 +115,7 @@ struct CtlLds {
   uint32_t sh[64];
   uint32_t wsum[NW];
   uint32_t count;
+  uint32_t wcnt[NW];      // per-wave counts of the tier-2 candidates
   uint64_t tlo;           // lower bound of the pair's k-th largest candidate
   uint64_t surv[64];      // candidates at or above it
   uint32_t nown;          // selected blocks of this chunk
@@ -851,25 +853,66 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (lane < kk) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
       }
     } else {
-      if (tid < nrows) L.u.keys[tid] = mykey;
+      // Two tiers (k > 64).  Tier 1: the chunk's kTier1 largest keys, largest
+      // first, in slots 0..kTier1-1, and its next largest key (the largest it
+      // leaves out of tier 1) in slot kTier1, from the one-wave path's sorts.
+      // Tier 2: the rest of its top k, in slots kTier1+1.., in row order.
+      // A reader whose pair's every slot kTier1 lies below the k-th largest
+      // tier-1 key needs tier 1 only.
+      const uint64_t srt = wave_sort_desc(mykey);
+      L.u.keys[tid] = srt;  // each wave's keys sorted: rows 0..nrows-1 hold the real ones
       __syncthreads();
-      if (k1 > 0) {
-        const uint64_t T1 = k1 == nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
-        if (tid == 0) L.count = 0u;
-        __syncthreads();
-        for (int i = tid; i < nrows; i += NT) {
-          const uint64_t key = L.u.keys[i];
-          if (key >= T1) cand.put_u64(chunk * s.kmax + (int)atomicAdd(&L.count, 1u), key);
-        }
+      if (wave == 0) {
+        uint64_t top = srt;
+        for (int v = 1; v < NW; ++v) top = wave_merge_desc(top, L.u.keys[64 * v + 63 - lane]);
+        if (lane <= kTier1) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, kTier1);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), kTier1);
+        if (lane == 0) L.tlo = k1 > kTier1 + 1 ? ((uint64_t)hi << 32) | lo : 0ull;  // tier 2 lies below it
       }
-      for (int e = k1 + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);  // below every real key
+      __syncthreads();
+      const uint64_t T1 = k1 >= nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
+      const uint64_t k_next = L.tlo;
+      const bool t2 = tid < nrows && mykey >= T1 && mykey < k_next;
+      const uint64_t bt = __ballot(t2);
+      if (lane == 0) L.wcnt[wave] = (uint32_t)__popcll(bt);
+      __syncthreads();
+      int pos = kTier1 + 1 + (int)__popcll(bt & ((1ull << lane) - 1ull));
+#pragma unroll
+      for (int v = 0; v < NW; ++v) pos += v < wave ? (int)L.wcnt[v] : 0;
+      if (t2) cand.put_u64(chunk * s.kmax + pos, mykey);
+      for (int e = max(k1, kTier1 + 1) + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);
     }
     __syncthreads();
     // the pair's top-k from every chunk's candidates
     CKV_MARK(chunk, 5);
     const int n2 = s.n_chunks * kk;
-    read_published(cand, n2, kk, s.kmax, L.u.keys, err);
-    __syncthreads();
+    // k > 64 with room to spare in tier 1: read tier 1 and the slots kTier1
+    // first; the full candidates only if some chunk may hold more
+    const bool tiered = !fast && s.n_chunks * kTier1 >= 2 * kk;
+    bool tier_ok = false;
+    uint64_t T_tier = 0;
+    if (tiered) {
+      const int n1 = s.n_chunks * kTier1;
+      uint64_t* nxt = L.u.keys + n1;  // [n_chunks] each chunk's slot kTier1
+      read_published(cand, n1, kTier1, s.kmax, L.u.keys, err);
+      const Coh cand_next(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax + kTier1,
+                          (size_t)s.n_chunks * s.kmax * 8 - kTier1 * 8, s.n_xcd > 0);
+      read_published(cand_next, s.n_chunks, 1, s.kmax, nxt, err);
+      __syncthreads();
+      T_tier = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n1, kk, L.hist, L.sh);
+      if (tid == 0) L.count = 0u;
+      __syncthreads();
+      for (int c = tid; c < s.n_chunks; c += NT)
+        if (nxt[c] > T_tier) atomicOr(&L.count, 1u);
+      __syncthreads();
+      tier_ok = L.count == 0u;  // every key left out of tier 1 lies below T_tier: it is the pair's T
+    }
+    if (!tier_ok) {
+      read_published(cand, n2, kk, s.kmax, L.u.keys, err);
+      __syncthreads();
+    }
+    const int nc = tier_ok ? s.n_chunks * kTier1 : n2;  // candidate keys in L.u.keys
     CKV_MARK(chunk, 6);
     if (fast) {
       // A lower bound of the k-th largest candidate: the k-th largest of the
@@ -928,16 +971,16 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       for (int e = tid; e < words; e += NT) L.bitmap[e] = 0u;
       __syncthreads();
       CKV_MARK(chunk, 12);
-      const uint64_t T = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
+      const uint64_t T = tier_ok ? T_tier : radix_kth_largest<NT>(LdsKeys{L.u.keys}, n2, kk, L.hist, L.sh);
       CKV_MARK(chunk, 13);
-      for (int e0 = tid; e0 < n2; e0 += 4 * NT) {  // four keys requested at a time
+      for (int e0 = tid; e0 < nc; e0 += 4 * NT) {  // four keys requested at a time
         uint64_t kb[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kb[u] = e0 + u * NT < n2 ? L.u.keys[e0 + u * NT] : 0ull;
+        for (int u = 0; u < 4; ++u) kb[u] = e0 + u * NT < nc ? L.u.keys[e0 + u * NT] : 0ull;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int idx = fused_key_index(kb[u]);
-          if (e0 + u * NT < n2 && kb[u] >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
+          if (e0 + u * NT < nc && kb[u] >= T && idx >= 0 && idx < M) atomicOr(&L.bitmap[idx >> 5], 1u << (idx & 31));
         }
       }
       __syncthreads();
@@ -969,15 +1012,15 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       n_own = (int)L.count;
       // The pair's selected blocks are attended to round robin over its chunks
       // in ascending order: this workgroup takes ranks chunk, chunk + n_chunks, ...
-      for (int e0 = tid; e0 < n2; e0 += 4 * NT) {  // four keys requested at a time
+      for (int e0 = tid; e0 < nc; e0 += 4 * NT) {  // four keys requested at a time
         uint64_t kb[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kb[u] = e0 + u * NT < n2 ? L.u.keys[e0 + u * NT] : 0ull;
+        for (int u = 0; u < 4; ++u) kb[u] = e0 + u * NT < nc ? L.u.keys[e0 + u * NT] : 0ull;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint64_t key = kb[u];
           const int idx = fused_key_index(key);
-          if (e0 + u * NT < n2 && key >= T && idx >= 0 && idx < M) {
+          if (e0 + u * NT < nc && key >= T && idx >= 0 && idx < M) {
             const int rank = (int)(L.hist[idx >> 5] + __popc(L.bitmap[idx >> 5] & ((1u << (idx & 31)) - 1u)));
             if (rank % s.n_chunks == chunk) {
               L.gblk[rank / s.n_chunks] = idx;

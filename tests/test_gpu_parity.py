@@ -11,7 +11,8 @@ from oracle import compkv_oracle as O
 
 from parity_util import (check_group_scores, check_outputs, check_selection_isolated,
                          check_selection_valid, check_selection_vs_oracle, check_summaries,
-                         check_workspace_clean, duplicated_blocks_case, run_gpu, run_oracle)
+                         check_workspace_clean, concentrated_blocks_case, duplicated_blocks_case, run_gpu,
+                         run_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +156,22 @@ def test_duplicated_blocks_tie_to_the_lowest_index(fused):
         assert np.all(rank[copies] == rank[copies[0]])
         assert ora[0].step.gaps[h] == 0.0
         np.testing.assert_array_equal(g.selected[0, h, :8], copies[:8])
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_selection_above_one_wave_with_a_concentrated_chunk(fused):
+    # k = 96 blocks over 8 chunks: the single launch first reads each chunk's
+    # 32 best candidates and its 33rd.  KV head 0 has 48 hot blocks in chunk 1,
+    # more than 32 of its top k, so its pair needs every candidate; KV head 1's
+    # pair is decided from the first 32 of every chunk.  Both against the
+    # oracle, in one launch.
+    w, hot = concentrated_blocks_case()
+    g, ora = full_check(w, budget=96 * 16, fused=fused)
+    rank = ora[0].step.rank_score[0]
+    top = np.argsort(-rank, kind="stable")[:96]
+    assert np.isin(hot, top).sum() > 32, "the hot chunk must hold more than 32 of the top k"
+    sel0 = g.selected[0, 0, :96]
+    assert np.isin(hot, sel0).sum() > 32
 
 
 def _dense_check(w):
