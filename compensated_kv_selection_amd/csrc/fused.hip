@@ -842,6 +842,24 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
                    s.n_xcd > 0);
     const int k1 = min(kk, nrows);
     const bool fast = kk <= 64;  // selections of up to one wave's width stay in registers
+    // k > 64 with room to spare in tier 1 (below): tier 2 is published only
+    // when the pair's tier 1 turns out not to hold its top k
+    const bool tiered = !fast && s.n_chunks * kTier1 >= 2 * kk && s.n_chunks * (2 * kTier1 + 2) <= kFusedCand;
+    // tier 2: the chunk's keys ranked kTier1 + 2 .. k1 (below k_next, its
+    // (kTier1 + 1)-th largest), into slots kTier1 + 1.., in row order, then
+    // sentinels up to slot k - 1; the chunk's keys are in L.u.keys[0..nrows)
+    auto publish_tier2 = [&](uint64_t k_next) {
+      const uint64_t T1 = k1 >= nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
+      const bool t2 = tid < nrows && mykey >= T1 && mykey < k_next;
+      const uint64_t bt = __ballot(t2);
+      if (lane == 0) L.wcnt[wave] = (uint32_t)__popcll(bt);
+      __syncthreads();
+      int pos = kTier1 + 1 + (int)__popcll(bt & ((1ull << lane) - 1ull));
+#pragma unroll
+      for (int v = 0; v < NW; ++v) pos += v < wave ? (int)L.wcnt[v] : 0;
+      if (t2) cand.put_u64(chunk * s.kmax + pos, mykey);
+      for (int e = max(k1, kTier1 + 1) + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);
+    };
     if (fast) {
       // each wave sorts its 64 blocks; wave 0 merges the four lists
       const uint64_t srt = wave_sort_desc(mykey);
@@ -857,8 +875,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       // first, in slots 0..kTier1-1, and its next largest key (the largest it
       // leaves out of tier 1) in slot kTier1, from the one-wave path's sorts.
       // Tier 2: the rest of its top k, in slots kTier1+1.., in row order.
-      // A reader whose pair's every slot kTier1 lies below the k-th largest
-      // tier-1 key needs tier 1 only.
+      // A pair whose every slot kTier1 lies below the k-th largest tier-1 key
+      // needs tier 1 only.
       const uint64_t srt = wave_sort_desc(mykey);
       L.u.keys[tid] = srt;  // each wave's keys sorted: rows 0..nrows-1 hold the real ones
       __syncthreads();
@@ -871,17 +889,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (lane == 0) L.tlo = k1 > kTier1 + 1 ? ((uint64_t)hi << 32) | lo : 0ull;  // tier 2 lies below it
       }
       __syncthreads();
-      const uint64_t T1 = k1 >= nrows ? 0 : radix_kth_largest<NT>(LdsKeys{L.u.keys}, nrows, k1, L.hist, L.sh);
-      const uint64_t k_next = L.tlo;
-      const bool t2 = tid < nrows && mykey >= T1 && mykey < k_next;
-      const uint64_t bt = __ballot(t2);
-      if (lane == 0) L.wcnt[wave] = (uint32_t)__popcll(bt);
-      __syncthreads();
-      int pos = kTier1 + 1 + (int)__popcll(bt & ((1ull << lane) - 1ull));
-#pragma unroll
-      for (int v = 0; v < NW; ++v) pos += v < wave ? (int)L.wcnt[v] : 0;
-      if (t2) cand.put_u64(chunk * s.kmax + pos, mykey);
-      for (int e = max(k1, kTier1 + 1) + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);
+      if (!tiered) publish_tier2(L.tlo);
     }
     __syncthreads();
     // the pair's top-k from every chunk's candidates
@@ -889,16 +897,22 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     const int n2 = s.n_chunks * kk;
     // k > 64 with room to spare in tier 1: read tier 1 and the slots kTier1
     // first; the full candidates only if some chunk may hold more
-    const bool tiered = !fast && s.n_chunks * kTier1 >= 2 * kk;
     bool tier_ok = false;
     uint64_t T_tier = 0;
     if (tiered) {
+      const uint64_t k_next = L.tlo;  // this chunk's (kTier1 + 1)-th largest key
+      // slots 0..kTier1 of every chunk in one read (staged past the packed
+      // arrays), then tier 1 packed and each chunk's slot kTier1 set aside
       const int n1 = s.n_chunks * kTier1;
-      uint64_t* nxt = L.u.keys + n1;  // [n_chunks] each chunk's slot kTier1
-      read_published(cand, n1, kTier1, s.kmax, L.u.keys, err);
-      const Coh cand_next(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax + kTier1,
-                          (size_t)s.n_chunks * s.kmax * 8 - kTier1 * 8, s.n_xcd > 0);
-      read_published(cand_next, s.n_chunks, 1, s.kmax, nxt, err);
+      uint64_t* nxt = L.u.keys + n1;              // [n_chunks] each chunk's slot kTier1
+      uint64_t* raw = nxt + s.n_chunks;           // [n_chunks][kTier1 + 1]
+      read_published(cand, s.n_chunks * (kTier1 + 1), kTier1 + 1, s.kmax, raw, err);
+      __syncthreads();
+      for (int e = tid; e < s.n_chunks * (kTier1 + 1); e += NT) {
+        const int c = e / (kTier1 + 1), i = e % (kTier1 + 1);
+        if (i < kTier1) L.u.keys[c * kTier1 + i] = raw[e];
+        else nxt[c] = raw[e];
+      }
       __syncthreads();
       T_tier = radix_kth_largest<NT>(LdsKeys{L.u.keys}, n1, kk, L.hist, L.sh);
       if (tid == 0) L.count = 0u;
@@ -907,6 +921,13 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (nxt[c] > T_tier) atomicOr(&L.count, 1u);
       __syncthreads();
       tier_ok = L.count == 0u;  // every key left out of tier 1 lies below T_tier: it is the pair's T
+      if (!tier_ok) {
+        // the same decision in every workgroup of the pair: each publishes
+        // its tier 2 now, then reads every candidate
+        if (tid < nrows) L.u.keys[tid] = mykey;
+        __syncthreads();
+        publish_tier2(k_next);
+      }
     }
     if (!tier_ok) {
       read_published(cand, n2, kk, s.kmax, L.u.keys, err);
