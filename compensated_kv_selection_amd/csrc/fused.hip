@@ -66,8 +66,8 @@ constexpr int NW = NT / 64;                // waves per workgroup
 // Phase trace, compiled only into a separately built library for timing
 // studies: thread 0 of a workgroup stores the constant-rate clock at mark i
 // into the sparse-step workspace's per-block score region, which the single
-// launch does not otherwise use (32 words per workgroup slot: marks below 16,
-// counts from 16; control slots 0..n_chunks-1, value slots n_chunks + chunk).
+// launch does not otherwise use (32 words per workgroup slot: marks below 24,
+// notes from 24; control slots 0..n_chunks-1, value slots n_chunks + chunk).
 // Needs that region to hold B * Hkv * 2 * n_chunks * 32 words (true for long
 // sequences).
 #define CKV_NOTE(slot, i, v)                                                                            \
@@ -76,7 +76,18 @@ constexpr int NW = NT / 64;                // waves per workgroup
       reinterpret_cast<uint64_t*>(w.xs)[((size_t)bg * (2 * s.n_chunks) + (slot)) * 32 + (i)] = (v);    \
   } while (0)
 #define CKV_MARK(slot, i) CKV_NOTE(slot, i, __builtin_amdgcn_s_memrealtime())
+// a slot's mark row, for marks set inside helpers
+#define CKV_ROW(slot) (reinterpret_cast<uint64_t*>(w.xs) + ((size_t)bg * (2 * s.n_chunks) + (slot)) * 32)
+#define CKV_ROW_MARK(row, i)                                                   \
+  do {                                                                          \
+    if (threadIdx.x == 0 && (row) != nullptr) (row)[i] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
 #else
+#define CKV_ROW(slot) nullptr
+#define CKV_ROW_MARK(row, i) \
+  do {                       \
+    (void)(row);             \
+  } while (0)
 #define CKV_NOTE(slot, i, v) \
   do {                       \
   } while (0)
@@ -222,7 +233,8 @@ __device__ __forceinline__ float read_tagged(const Coh& src, int i, uint64_t v, 
 // layout and tag) is folded in first.
 template <int D, int G>
 __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8], float (*red)[G][D + 4],
-                                const Coh& part, uint32_t tag, const Coh* extra, uint32_t* err) {
+                                const Coh& part, uint32_t tag, const Coh* extra, uint32_t* err,
+                                uint64_t* trace_row = nullptr) {
   constexpr int LPR = D / 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = tid % LPR;
   // the other partial's words for this thread's first output, requested
@@ -262,6 +274,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
     }
   }
   __syncthreads();
+  CKV_ROW_MARK(trace_row, 10);
   for (int o = tid; o < G * D / 2; o += NT) {
     const int j = o / (D / 2), d2 = o % (D / 2);
     float Mx = -INFINITY;
@@ -291,6 +304,7 @@ __device__ void publish_partial(float (&m)[G], float (&l)[G], float (&acc)[G][8]
       a1 = a1 * f1 + e1 * f2;
       Ls = Ls * f1 + le * f2;
       Mx = M;
+      if (o == tid) CKV_ROW_MARK(trace_row, 15);
     }
     part.put_u64(h + 2 + 2 * d2, tagged(a0, tag));
     part.put_u64(h + 3 + 2 * d2, tagged(a1, tag));
@@ -1137,7 +1151,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   // they are folded into this partial, so the merge reads one per chunk
   const Coh vpart(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
                   (size_t)G * (D + 2) * 8, s.n_xcd > 0);
-  publish_partial<D, G>(m, l, acc, L.u.red, part, tag, &vpart, err);
+  publish_partial<D, G>(m, l, acc, L.u.red, part, tag, &vpart, err, CKV_ROW(chunk));
   CKV_MARK(chunk, 9);
   CKV_NOTE(chunk, 26, __builtin_amdgcn_s_memtime());
 
@@ -1297,6 +1311,7 @@ __device__ void merge_slice(const Shape& s, const StepIO& io, const Work& w, int
       L.pa[it] = a;
     }
     __syncthreads();
+    if (base == o0) CKV_MARK(slot, 16);
     for (int oo = wave; oo < nout; oo += NW) {
       const int o = base + oo;
       const int j = o / (D / 4), d4 = o % (D / 4);

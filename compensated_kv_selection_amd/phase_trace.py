@@ -33,7 +33,8 @@ CONTROL = {0: "entry", 1: "q staged", 2: "mean keys scored", 3: "header and weig
            4: "headers read", 5: "candidates published", 6: "candidates read",
            12: "radix select: start", 13: "radix select: T known", 14: "selected blocks counted",
            7: "selection known",
-           8: "exact attention done", 9: "partial published", 11: "merged (output written)"}
+           8: "exact attention done", 10: "partial: reductions done", 15: "partial: value sums read",
+           9: "partial published", 16: "merge: every partial read", 11: "merged (output written)"}
 VALUE = {0: "entry", 1: "weights read", 2: "mean values summed", 3: "partial published"}
 
 
@@ -92,7 +93,7 @@ def main(argv=None) -> int:
     n = pairs * 2 * nch * MARKS_PER_SLOT
     words = ws[ctrl_bytes: ctrl_bytes + 8 * n].view(torch.int64).cpu().numpy().reshape(pairs, 2 * nch,
                                                                                       MARKS_PER_SLOT)
-    times = words[:, :, :16]
+    times = words[:, :, :24]  # marks; counts and notes from 24
     t0 = times[:, :nch, 0][times[:, :nch, 0] > 0].min()
     us = (times.astype(np.float64) - t0) * 1e-2  # 100 MHz ticks
 
