@@ -416,45 +416,25 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rs = tid / LPR, c = tid % LPR;  // row slot, 8-channel slice
-  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
-  const int M = (Lseq + s.bs - 1) / s.bs;
-  const int kk = min(M, s.kmax);
-  const bool ranked = kk > 0 && kk < M;
-  const bool need_mu = kk < M;  // logits of omitted blocks are needed
-  const bool comp = need_mu && io.compensate;
   const int start = chunk * kChunk;
-  const int nrows = max(0, min(M, start + kChunk) - start);
   const size_t row0 = (size_t)bg * s.max_blocks + start;  // logical summary row of the chunk
   const KV* mk = static_cast<const KV*>(io.summ.mean_k) + row0 * D;
   const KV* mv = static_cast<const KV*>(io.summ.mean_v) + row0 * D;
   const int r = s.r, gs = D / r;
   const float* gv = io.summ.gvar + row0 * r;
   uint32_t* err = w.ctrl + 2;
-  // Decode append (kApp): the sequence's last token is new.  The control
-  // workgroup of the chunk holding its block (row ti of the chunk, tn tokens)
-  // writes it into its page slot and recomputes the block's summary, with
-  // the same arithmetic as the summary build; nobody reads that slot before.
-  static_assert(!kApp || (MF && kR4 && D == 128), "the appending instance is bf16, d = 128, r = 4");
-  bool app = false;
-  int tpage = -1, tn = 0, ti = 0;
-  if constexpr (kApp) {
-    if (M > 0 && chunk == (M - 1) / kChunk) {
-      tpage = ld_uniform(io.block_table + (size_t)b * s.max_blocks + M - 1);
-      app = tpage >= 0 && tpage < s.P;
-      tn = Lseq - (M - 1) * s.bs;
-      ti = M - 1 - start;
-    }
-  }
 
-  CKV_MARK(chunk, 0);
-  CKV_NOTE(chunk, 25, __builtin_amdgcn_s_memtime());
   // ---- loads, all issued at once, oldest first: q, page-table entries, the
   // matrix-operand rows of q, then the chunk's mean keys and variances.
-  // Buffer views end at the chunk's last block, so rows past it read 0. ----
+  // They do not wait for the sequence length: the views end at the chunk's
+  // last row of the summary store (max_blocks rows per pair, all allocated),
+  // rows at or past the sequence's end are read but never used, and rows
+  // past the store read 0. ----
+  const int nmax = max(0, min(s.max_blocks, start + kChunk) - start);
   const Buf qb(static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D, G * D * sizeof(KV));
-  const Buf btb(io.block_table + (size_t)b * s.max_blocks + start, kk > 0 ? nrows * 4 : 0);
-  const Buf mkb(mk, need_mu ? nrows * D * sizeof(KV) : 0);
-  const Buf gvb(gv, need_mu && ranked ? nrows * r * 4 : 0);
+  const Buf btb(io.block_table + (size_t)b * s.max_blocks + start, nmax * 4);
+  const Buf mkb(mk, MF ? nmax * D * sizeof(KV) : 0);
+  const Buf gvb(gv, nmax * r * 4);
   Raw8<KV> qraw;
   raw_load(qb, tid * 8, qraw);  // threads past G * D / 8 read 0
   const int pge = (int)btb.u32(4 * tid);
@@ -499,6 +479,32 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       }
     }
   }
+
+  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
+  const int M = (Lseq + s.bs - 1) / s.bs;
+  const int kk = min(M, s.kmax);
+  const bool ranked = kk > 0 && kk < M;
+  const bool need_mu = kk < M;  // logits of omitted blocks are needed
+  const bool comp = need_mu && io.compensate;
+  const int nrows = max(0, min(M, start + kChunk) - start);
+  // Decode append (kApp): the sequence's last token is new.  The control
+  // workgroup of the chunk holding its block (row ti of the chunk, tn tokens)
+  // writes it into its page slot and recomputes the block's summary, with
+  // the same arithmetic as the summary build; nobody reads that slot before.
+  static_assert(!kApp || (MF && kR4 && D == 128), "the appending instance is bf16, d = 128, r = 4");
+  bool app = false;
+  int tpage = -1, tn = 0, ti = 0;
+  if constexpr (kApp) {
+    if (M > 0 && chunk == (M - 1) / kChunk) {
+      tpage = ld_uniform(io.block_table + (size_t)b * s.max_blocks + M - 1);
+      app = tpage >= 0 && tpage < s.P;
+      tn = Lseq - (M - 1) * s.bs;
+      ti = M - 1 - start;
+    }
+  }
+
+  CKV_MARK(chunk, 0);
+  CKV_NOTE(chunk, 25, __builtin_amdgcn_s_memtime());
   // q rows to LDS; partial |q|^2 of each thread's 8 channels
   {
     float x[8];
@@ -1259,6 +1265,10 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
   }
   CKV_MARK(s.n_chunks + chunk, 2);
+  // Written through: these sums are needed late, and every line left dirty
+  // in L2 is written back when the launch ends, which the next launch waits
+  // for.  (Stores and loads share one counter, so the control workgroups,
+  // which wait on loads after their stores, keep the default policy.)
   const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
                  (size_t)G * (D + 2) * 8, s.n_xcd > 0);
   publish_partial<D, G>(m, l, acc, L.red, part, tag, nullptr, err);

@@ -46,6 +46,10 @@
  *   block_size] and skip page ids outside [0, num_pages) and block ids
  *   outside [0, num_blocks), so invalid contents give unspecified results
  *   but never an out-of-bounds access.
+ * - A step may read a pair's whole row of block_table and summaries (all
+ *   max_blocks_per_seq entries, which the layouts below allocate) before
+ *   it knows seq_lens; entries past a sequence's end are never used, so
+ *   they may hold anything.
  * - Inputs must be finite; non-finite inputs give unspecified results.
  * - The library is reentrant; calls on different streams with disjoint
  *   outputs and workspaces may overlap, except that the single launch of

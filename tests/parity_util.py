@@ -312,18 +312,19 @@ def duplicated_blocks_case(seed: int = 77, seq_len: int = 140000, n_copies: int 
     return w, copies
 
 
-def concentrated_blocks_case(seed: int = 91, n_hot: int = 48, hot_chunk: int = 1) -> tuple:
-    """A 2-KV-head, 4-query-heads-per-KV-head bf16 workload of 8 chunks (2048
-    blocks).  For KV head 0 only, n_hot blocks of one chunk carry keys along
-    the group's mean query with a wide spread (large mass and large
-    within-block variance), so that they top the ranking; KV
-    head 1 keeps i.i.d. keys with 8 ordinary needles.  With a budget of 96
-    blocks, KV head 0's pair has a chunk holding more of its top k than the
-    chunk's first candidates, and KV head 1's pair does not.  Returns (inputs,
-    the hot blocks)."""
-    w = W.make_decode_inputs(name="concentrated", seq_lens=[2048 * 16], num_q_heads=8, num_kv_heads=2,
-                             head_dim=128, r_groups=4, budget_tokens=96 * 16, dtype="bf16", n_needles=8,
-                             n_outliers=2, seed=seed)
+def concentrated_blocks_case(seed: int = 91, n_hot: int = 48, hot_chunk: int = 1, n_blocks: int = 2048,
+                             budget_blocks: int = 96) -> tuple:
+    """A 2-KV-head, 4-query-heads-per-KV-head bf16 workload of n_blocks
+    blocks (by default 8 chunks of 256).  For KV head 0 only, n_hot blocks of
+    one chunk carry keys along the group's mean query with a wide spread
+    (large mass and large within-block variance), so that they top the
+    ranking; KV head 1 keeps i.i.d. keys with 8 ordinary needles.  With a
+    budget of 96 blocks, KV head 0's pair has a chunk holding more of its top
+    k than the chunk's first candidates, and KV head 1's pair does not.
+    Returns (inputs, the hot blocks)."""
+    w = W.make_decode_inputs(name="concentrated", seq_lens=[n_blocks * 16], num_q_heads=8, num_kv_heads=2,
+                             head_dim=128, r_groups=4, budget_tokens=budget_blocks * 16, dtype="bf16",
+                             n_needles=8, n_outliers=2, seed=seed)
     rng = np.random.default_rng(seed + 1)
     hot = np.sort(rng.choice(np.arange(hot_chunk * 256, (hot_chunk + 1) * 256), size=n_hot, replace=False))
     k = w.k_tokens[0]

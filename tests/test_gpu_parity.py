@@ -174,6 +174,23 @@ def test_selection_above_one_wave_with_a_concentrated_chunk(fused):
     assert np.isin(hot, sel0).sum() > 32
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_selection_of_32_with_a_concentrated_chunk(fused):
+    # k = 32 blocks over 16 chunks.  KV head 0 has 20 hot blocks in chunk 5,
+    # more than 8 of its top k, so its chunk's candidates reach deep into the
+    # pair's selection; KV head 1's selection is spread, no chunk holding
+    # more than 8.  Both against the oracle, in one launch.
+    w, hot = concentrated_blocks_case(seed=93, n_hot=20, hot_chunk=5, n_blocks=4096, budget_blocks=32)
+    if fused:
+        assert C.decode_step_launches(dims_of(w), 32 * 16) == 1
+    g, ora = full_check(w, budget=32 * 16, fused=fused)
+    top0 = np.argsort(-ora[0].step.rank_score[0], kind="stable")[:32]
+    assert np.isin(hot, top0).sum() > 8, "the hot chunk must hold more than 8 of the top k"
+    top1 = np.argsort(-ora[0].step.rank_score[1], kind="stable")[:32]
+    assert np.bincount(top1 // 256, minlength=16).max() <= 8
+    assert np.isin(hot, g.selected[0, 0, :32]).sum() > 8
+
+
 def _dense_check(w):
     print(f"[case] dense {w.name} seed={w.seed} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
           f"d={w.head_dim} {w.dtype} lens={list(w.seq_lens)[:6]}", flush=True)
