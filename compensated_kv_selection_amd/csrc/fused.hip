@@ -1265,10 +1265,6 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     }
   }
   CKV_MARK(s.n_chunks + chunk, 2);
-  // Written through: these sums are needed late, and every line left dirty
-  // in L2 is written back when the launch ends, which the next launch waits
-  // for.  (Stores and loads share one counter, so the control workgroups,
-  // which wait on loads after their stores, keep the default policy.)
   const Coh part(w.fpart + ((size_t)bg * 2 * s.n_chunks + s.n_chunks + chunk) * G * (D + 2),
                  (size_t)G * (D + 2) * 8, s.n_xcd > 0);
   publish_partial<D, G>(m, l, acc, L.red, part, tag, nullptr, err);
