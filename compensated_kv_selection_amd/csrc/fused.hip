@@ -20,17 +20,21 @@
 //   a control workgroup loads the chunk's mean keys, grouped variances and
 //     page-table entries, computes the block-mean logits on the matrix cores
 //     (the G query heads are the rows of a 16x16x32 bf16 MFMA tile),
-//     publishes the chunk's compensation weights and header (max logit,
-//     partial Z_hat per head), reads every header of the pair, ranks the
+//     publishes the chunk's header (max logit, partial Z_hat per head; for
+//     f32 and the appending instance also its compensation weights), reads
+//     every header of the pair, ranks the
 //     chunk's blocks, publishes the chunk's top-k candidates, reads every
 //     candidate of the pair, finds the pair's top-k, attends exactly to its
 //     share of the selected blocks (ranks chunk, chunk + n_chunks, ... of the
 //     pair's selection), takes back the compensation terms of the selected
 //     blocks of its chunk, folds in the chunk's value sums and publishes
 //     one (max, sum, acc[d]) partial per query head;
-//   a value workgroup waits for a chunk's weights, streams the chunk's mean
-//     values, sums the compensation terms of all the chunk's blocks and
-//     publishes them for the chunk's control workgroup.
+//   a value workgroup forms the chunk's compensation weights n e^{s_bar - max}
+//     itself (bf16 without append: the same matrix-core logits from the same
+//     mean keys, which the control workgroup's loads bring into L2, so the
+//     same bits; otherwise it waits for the control workgroup's), streams the
+//     chunk's mean values, sums the compensation terms of all the chunk's
+//     blocks and publishes them for the chunk's control workgroup.
 // Then every control workgroup of the pair merges its slice of the pair's
 // output from the control workgroups' partials, and chunk 0's advances the
 // pair's epoch.
@@ -140,6 +144,8 @@ struct ValLds {
   float w[G][kChunk];
   float mx[G];
   float red[NW][G][D + 4];
+  float sb[G][kChunk];          // bf16 without append: the block-mean logits, formed here
+  uint4 stage[NW][16 * D / 8];  //   through the same matrix-operand tiles as the control's
 };
 
 template <int D, int G>
@@ -412,6 +418,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   constexpr int LPR = D / 8, RS = NT / LPR;
   constexpr int KT = D / 32, CPR = D / 8, RPI = 64 / CPR, NMU = CPR;  // NMU: 64 rows per wave / RPI
   constexpr bool MF = std::is_same<KV, uint16_t>::value;
+  constexpr bool kOwnW = MF && !kApp;  // the value workgroups form the weights themselves
   const int b = bg / s.Hkv, g = bg % s.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -797,7 +804,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         z = fmaf(wt, 1.f + half, z);
         L.wt[j][ri] = wt;
         L.lam[j][ri] = io.score_mode == kScoreMass ? sb + flog(massf) : sb + flog(massf * half);
-        if (comp) wts.put_u64(j * kWStride + ri, tagged(wt, tag));
+        if (comp && !kOwnW) wts.put_u64(j * kWStride + ri, tagged(wt, tag));
       }
       z = wave_sum_dpp(z);
       if (lane == 0) {
@@ -808,7 +815,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
           // before head 0's chunk max, after which the value workgroup reads it
           if (app && j == 0) __builtin_amdgcn_s_waitcnt(0);
         }
-        if (comp) wts.put_u64(j * kWStride + kChunk, tagged(mx, tag));
+        if (comp && !kOwnW) wts.put_u64(j * kWStride + kChunk, tagged(mx, tag));
       }
     }
   }
@@ -1192,12 +1199,18 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 // Value workgroup of chunk `chunk` of pair bg: the compensation terms of every
 // block of the chunk, n e^{s_bar} mean_v, with the control workgroup's weights.
 // ---------------------------------------------------------------------------
-template <typename KV, int D, int G>
+template <typename KV, int D, int G, bool kApp>
 __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int bg, int chunk, uint32_t tag,
                           ValLds<D, G>& L) {
   constexpr int LPR = D / 8, RS = NT / LPR, RPL = kChunk / RS;
-  const int b = bg / s.Hkv;
-  const int tid = threadIdx.x;
+  constexpr int KT = D / 32, CPR = D / 8, RPI = 64 / CPR, NMU = CPR;
+  // bf16 without append: the weights are formed here from the chunk's mean
+  // keys (in L2, which the control workgroup's loads of the same rows fill),
+  // with the control workgroup's arithmetic and so its bits; no hand-off
+  constexpr bool kOwn = std::is_same<KV, uint16_t>::value && !kApp;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rs = tid / LPR, c = tid % LPR;
   const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
   const int M = (Lseq + s.bs - 1) / s.bs;
@@ -1218,7 +1231,61 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
-  if (comp) {
+  if (comp && kOwn) {
+    const Buf qb(static_cast<const KV*>(io.q) + ((size_t)b * s.Hq + g * G) * D, G * D * sizeof(KV));
+    const Buf mkb(static_cast<const KV*>(io.summ.mean_k) + ((size_t)bg * s.max_blocks + start) * D,
+                  nrows * D * sizeof(KV));
+    bf16x8_t qa[KT];
+    uint4 mu[NMU];
+    const int head = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      qa[kt] = __builtin_bit_cast(bf16x8_t, qb.u128(2 * (head * D + 32 * kt + 8 * kq)));  // 0 past G
+#pragma unroll
+    for (int u = 0; u < NMU; ++u) {
+      const int row = 64 * wave + RPI * u + lane / CPR;
+      mu[u] = mkb.u128(2 * (row * D + (lane % CPR) * 8));
+    }
+    uint4* st = L.stage[wave];
+    const bool holder = (lane >> 4) * 4 < G;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+#pragma unroll
+      for (int v = 0; v < 16 / RPI; ++v) {
+        const int rr = RPI * v + lane / CPR, ch = lane % CPR;
+        st[rr * CPR + (ch ^ (rr & (CPR - 1)))] = mu[g4 * (16 / RPI) + v];
+      }
+      __builtin_amdgcn_wave_barrier();
+      f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int rr = lane & 15, ch = 4 * kt + (lane >> 4);
+        const uint4 bv = st[rr * CPR + (ch ^ (rr & (CPR - 1)))];
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kt], __builtin_bit_cast(bf16x8_t, bv), a4, 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int ri = 64 * wave + 16 * g4 + (lane & 15);
+      if (ri < nrows && holder) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * (lane >> 4) + i;
+          if (j < G) L.sb[j][ri] = a4[i] * s.tau;
+        }
+      }
+    }
+    __syncthreads();
+    for (int j = wave; j < G; j += NW) {
+      float mx = -INFINITY;
+      for (int ri = lane; ri < nrows; ri += 64) mx = fmaxf(mx, L.sb[j][ri]);
+      mx = wave_max_dpp(mx);
+      for (int ri = lane; ri < nrows; ri += 64) {
+        const int n = min(s.bs, Lseq - (start + ri) * s.bs);
+        L.w[j][ri] = (float)n * fexp(L.sb[j][ri] - mx);
+      }
+      if (lane == 0) L.mx[j] = mx;
+    }
+    __syncthreads();
+  } else if (comp) {
     const Coh wts(w.fw + ((size_t)bg * s.n_chunks + chunk) * G * kWStride, (size_t)G * kWStride * 8, s.n_xcd > 0);
     uint32_t spins = 0;
     if (tid < G) L.mx[tid] = read_tagged(wts, tid * kWStride + kChunk, wts.u64(tid * kWStride + kChunk), tag, spins, err);
@@ -1232,6 +1299,8 @@ __device__ void val_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       for (int j = 0; j < G; ++j) L.w[j][tid] = read_tagged(wts, j * kWStride + tid, wv[j], tag, spins, err);
     }
     __syncthreads();
+  }
+  if (comp) {
 #pragma unroll
     for (int j = 0; j < G; ++j) m[j] = L.mx[j];
     CKV_MARK(s.n_chunks + chunk, 1);
@@ -1421,7 +1490,7 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s_arg, StepIO i
     } else {
       // value workgroup v sums chunks v, v + n_val, ... in turn
       for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
-        val_chunk<KV, D, G>(s, io, w, bg, chunk, epoch + 1u, lds.v);
+        val_chunk<KV, D, G, kApp>(s, io, w, bg, chunk, epoch + 1u, lds.v);
         __syncthreads();
       }
       // then clear its chunks' rows of the previous call's headers and
