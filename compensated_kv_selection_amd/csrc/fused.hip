@@ -99,6 +99,7 @@ constexpr int NW = NT / 64;                // waves per workgroup
 #endif
 
 constexpr int kTier1 = 32;  // k > 64: each chunk's candidates read first (plus the next key)
+constexpr int kCtrlTail = 4;  // per-pair control words 4-5: the appended tail summary is stored (tagged)
 constexpr int kPollBatch = 8;              // published words read per thread per round trip
 constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
 constexpr int kWStride = kChunk + 1;       // tagged words per head: weights, then the chunk max
@@ -146,6 +147,8 @@ struct ValLds {
   float red[NW][G][D + 4];
   float sb[G][kChunk];          // bf16 without append: the block-mean logits, formed here
   uint4 stage[NW][16 * D / 8];  //   through the same matrix-operand tiles as the control's
+  uint4 tmk[D / 8];             // decode append: the tail block's new mean key (stored bits)
+  float tmv[D];                 //   and mean value, as stored
 };
 
 template <int D, int G>
@@ -494,18 +497,18 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   const bool need_mu = kk < M;  // logits of omitted blocks are needed
   const bool comp = need_mu && io.compensate;
   const int nrows = max(0, min(M, start + kChunk) - start);
-  // Decode append (kApp): the sequence's last token is new.  The control
-  // workgroup of the chunk holding its block (row ti of the chunk, tn tokens)
-  // writes it into its page slot and recomputes the block's summary, with
-  // the same arithmetic as the summary build; nobody reads that slot before.
+  // Decode append (kApp): the sequence's last token is new.  The value
+  // workgroup of the chunk holding its block (row ti of the chunk) writes it
+  // into its page slot and recomputes and stores the block's summary
+  // (append_tail); this control workgroup reads that summary back and forms
+  // the row's logits again.
   static_assert(!kApp || (MF && kR4 && D == 128), "the appending instance is bf16, d = 128, r = 4");
   bool app = false;
-  int tpage = -1, tn = 0, ti = 0;
+  int ti = 0;
   if constexpr (kApp) {
     if (M > 0 && chunk == (M - 1) / kChunk) {
-      tpage = ld_uniform(io.block_table + (size_t)b * s.max_blocks + M - 1);
+      const int tpage = ld_uniform(io.block_table + (size_t)b * s.max_blocks + M - 1);
       app = tpage >= 0 && tpage < s.P;
-      tn = Lseq - (M - 1) * s.bs;
       ti = M - 1 - start;
     }
   }
@@ -543,27 +546,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   }
   __syncthreads();
   CKV_MARK(chunk, 1);
-  // decode append: row rs, slice c of the tail page's keys and values (16
-  // rows x 16 slices), the new token's row taken from k_new / v_new (the
-  // page slot it goes to is never read)
-  Raw8<KV> tkr, tvr;
-  if constexpr (kApp) {
-    if (app) {
-      const KV* ks;
-      const KV* vs;
-      if (rs == tn - 1) {
-        const size_t o = ((size_t)b * s.Hkv + g) * D + c * 8;
-        ks = static_cast<const KV*>(io.k_new) + o;
-        vs = static_cast<const KV*>(io.v_new) + o;
-      } else {
-        const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
-        ks = static_cast<const KV*>(io.k_cache) + o;
-        vs = static_cast<const KV*>(io.v_cache) + o;
-      }
-      raw_load(ks, tkr);
-      raw_load(vs, tvr);
-    }
-  }
 
   // ---- block-mean logits and variance estimates ----
   if (need_mu) {
@@ -672,74 +654,37 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
   __syncthreads();
   CKV_MARK(chunk, 2);
 
-  // ---- decode append: the tail block's summary, stores, and its logits again ----
+  // ---- decode append: the tail block's new summary, then its logits again ----
   if constexpr (kApp) {
     if (app) {
-      L.u.stage[0][tid] = tkr.a;  // row rs, slice c: row-major, channels in order
-      L.u.stage[1][tid] = tvr.a;
-      if (rs == tn - 1) {  // the new token into its page slot
-        const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
-        raw_store(static_cast<KV*>(const_cast<void*>(io.k_cache)) + o, tkr);
-        raw_store(static_cast<KV*>(const_cast<void*>(io.v_cache)) + o, tvr);
-      }
-      __syncthreads();
-      // one channel per thread (keys, then values), each with the summary
-      // build's arithmetic and order for that channel
-      float* tvar = reinterpret_cast<float*>(L.u.stage[2]);  // per-channel key sums of squares
-      {
-        const bool isv = tid >= D;
-        const int ch = tid & (D - 1);
-        const uint16_t* rows = reinterpret_cast<const uint16_t*>(L.u.stage[isv ? 1 : 0]) + ch;
-        const float x0 = __uint_as_float((uint32_t)rows[0] << 16);
-        float sx = 0.f;
-#pragma unroll
-        for (int t = 1; t < kBlockSize; ++t)
-          if (t < tn) sx += __uint_as_float((uint32_t)rows[t * D] << 16) - x0;
-        const float mu = x0 + sx / (float)tn;
-        const uint32_t mb = bf16_rne(mu);
-        if (isv) {
-          L.tmv[ch] = __uint_as_float(mb << 16);
-        } else {
-          reinterpret_cast<uint16_t*>(L.tmk)[ch] = (uint16_t)mb;
-          float var = 0.f;
-#pragma unroll
-          for (int t = 0; t < kBlockSize; ++t) {
-            if (t < tn) {
-              const float dl = __uint_as_float((uint32_t)rows[t * D] << 16) - mu;
-              var = fmaf(dl, dl, var);
-            }
-          }
-          tvar[ch] = var;
-        }
+      // the tail chunk's value workgroup wrote the new token into its page
+      // slot and the block's new summary, then raised the pair's tail word
+      const Coh tw(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + kCtrlTail, 8, s.n_xcd > 0);
+      if (tid == 0) {
+        uint32_t spins = 0;
+        read_tagged(tw, 0, tw.u64(0), tag, spins, err);
+        tw.put_u64(0, 0u);  // the word's only reader: it ends the call zero
       }
       __syncthreads();
       const size_t srow = (size_t)bg * s.max_blocks + M - 1;
+      const Coh smk(static_cast<const KV*>(io.summ.mean_k) + srow * D, D * sizeof(KV), false);
+      const Coh smv(static_cast<const KV*>(io.summ.mean_v) + srow * D, D * sizeof(KV), false);
+      const Coh sgv(io.summ.gvar + srow * 4, 16, false);
       if (tid < LPR) {
-        *reinterpret_cast<uint4*>(static_cast<KV*>(io.summ.mean_k) + srow * D + tid * 8) = L.tmk[tid];
+        const float4 v = smk.f32x4(4 * tid);
+        L.tmk[tid] = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                __float_as_uint(v.w));
       } else if (tid < 2 * LPR) {
-        const float* tv = L.tmv + (tid - LPR) * 8;
-        uint4 wb;
-        wb.x = (__float_as_uint(tv[0]) >> 16) | (__float_as_uint(tv[1]) & 0xffff0000u);
-        wb.y = (__float_as_uint(tv[2]) >> 16) | (__float_as_uint(tv[3]) & 0xffff0000u);
-        wb.z = (__float_as_uint(tv[4]) >> 16) | (__float_as_uint(tv[5]) & 0xffff0000u);
-        wb.w = (__float_as_uint(tv[6]) >> 16) | (__float_as_uint(tv[7]) & 0xffff0000u);
-        *reinterpret_cast<uint4*>(static_cast<KV*>(io.summ.mean_v) + srow * D + (tid - LPR) * 8) = wb;
-      } else if (tid < 2 * LPR + 4) {
-        // group t of 32 channels: each 8-channel slice summed in order, then
-        // the four slices pairwise, as the build sums across its lanes
-        const int t = tid - 2 * LPR;
-        float sl[4];
+        const float4 v = smv.f32x4(4 * (tid - LPR));
+        const uint32_t wv[4] = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                __float_as_uint(v.w)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sl[i] = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sl[i] += tvar[(4 * t + i) * 8 + e];
+        for (int e = 0; e < 4; ++e) {
+          L.tmv[(tid - LPR) * 8 + 2 * e] = __uint_as_float(wv[e] << 16);
+          L.tmv[(tid - LPR) * 8 + 2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
         }
-        const float gvv = ((sl[0] + sl[1]) + (sl[2] + sl[3])) / ((float)tn * (float)(D / 4));
-        io.summ.gvar[srow * 4 + t] = gvv;
-        L.tgv[t] = gvv;
-      } else if (tid == 2 * LPR + 4 && g == 0) {
-        io.summ.count[(size_t)b * s.max_blocks + M - 1] = tn;
+      } else if (tid < 2 * LPR + 4) {
+        L.tgv[tid - 2 * LPR] = sgv.f32(tid - 2 * LPR);
       }
       __syncthreads();
       if (need_mu && wave == ti / 64) {
@@ -810,11 +755,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       if (lane == 0) {
         L.mx[j] = mx;
         if (ranked) hdr.put_u64(chunk * G + j, ((uint64_t)__float_as_uint(z) << 32) | __float_as_uint(mx));
-        if constexpr (kApp) {
-          // decode append: wave 0 stored the new summary row; it is in L2
-          // before head 0's chunk max, after which the value workgroup reads it
-          if (app && j == 0) __builtin_amdgcn_s_waitcnt(0);
-        }
         if (comp && !kOwnW) wts.put_u64(j * kWStride + kChunk, tagged(mx, tag));
       }
     }
@@ -858,11 +798,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (lam != -INFINITY && lz != -INFINITY) S += fexp(lam - lz);
       }
       mykey = fused_key(S, start + tid, L.pgt[tid]);
-    }
-    // decode append: the new token's rows are in L2 before any candidate
-    // that leads another workgroup to them is published
-    if constexpr (kApp) {
-      if (app) __builtin_amdgcn_s_waitcnt(0);
     }
     // the chunk's top-k candidates, published largest first
     const Coh cand(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8,
@@ -1085,9 +1020,6 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     n_gather = nrows;
     L.gblk[tid] = start + tid;
     L.gpg[tid] = L.pgt[tid];
-    if constexpr (kApp) {
-      if (app) __builtin_amdgcn_s_waitcnt(0);  // the new token's rows, read back below
-    }
     __syncthreads();
   }
 
@@ -1192,6 +1124,120 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       } else
         for (int i = tid; i < kk; i += NT) out[i] = i;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode append, run by the value workgroup that sums the tail chunk of pair
+// bg before it starts on any chunk: the sequence's last token (row tn - 1 of
+// its tail block, in page tpage) is new.  Its key and value rows go into
+// their page slot, and the tail block's summary (mean key and value,
+// grouped variances, count) is recomputed from the page with the summary
+// build's arithmetic and stored; then the pair's tail word is raised with
+// this call's tag.  The tail chunk's control workgroup waits for that word
+// and reads the summary back.
+// ---------------------------------------------------------------------------
+template <typename KV, int D, int G>
+__device__ void append_tail(const Shape& s, const StepIO& io, const Work& w, int bg, uint32_t tag, ValLds<D, G>& L) {
+  static_assert(std::is_same<KV, uint16_t>::value && D == 128, "the appending instance is bf16, d = 128");
+  constexpr int LPR = D / 8;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int tid = threadIdx.x;
+  const int rs = tid / LPR, c = tid % LPR;  // row rs, 8-channel slice c of the 16-row page
+  const int Lseq = clamp_len(ld_uniform(io.seq_lens + b), s.max_blocks * s.bs);
+  const int M = (Lseq + s.bs - 1) / s.bs;
+  if (M == 0) return;
+  const int tpage = ld_uniform(io.block_table + (size_t)b * s.max_blocks + M - 1);
+  if (tpage < 0 || tpage >= s.P) return;
+  const int tn = Lseq - (M - 1) * s.bs;
+  // row rs, slice c of the tail page's keys and values, the new token's row
+  // taken from k_new / v_new (the page slot it goes to is not read)
+  Raw8<KV> tkr, tvr;
+  {
+    const KV* ks;
+    const KV* vs;
+    if (rs == tn - 1) {
+      const size_t o = ((size_t)b * s.Hkv + g) * D + c * 8;
+      ks = static_cast<const KV*>(io.k_new) + o;
+      vs = static_cast<const KV*>(io.v_new) + o;
+    } else {
+      const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
+      ks = static_cast<const KV*>(io.k_cache) + o;
+      vs = static_cast<const KV*>(io.v_cache) + o;
+    }
+    raw_load(ks, tkr);
+    raw_load(vs, tvr);
+  }
+  L.stage[0][tid] = tkr.a;  // row rs, slice c: row-major, channels in order
+  L.stage[1][tid] = tvr.a;
+  if (rs == tn - 1) {  // the new token into its page slot
+    const size_t o = (((size_t)tpage * s.Hkv + g) * s.bs + rs) * D + c * 8;
+    raw_store(static_cast<KV*>(const_cast<void*>(io.k_cache)) + o, tkr);
+    raw_store(static_cast<KV*>(const_cast<void*>(io.v_cache)) + o, tvr);
+  }
+  __syncthreads();
+  // one channel per thread (keys, then values), each with the summary
+  // build's arithmetic and order for that channel
+  float* tvar = reinterpret_cast<float*>(L.stage[2]);  // per-channel key sums of squares
+  {
+    const bool isv = tid >= D;
+    const int ch = tid & (D - 1);
+    const uint16_t* rows = reinterpret_cast<const uint16_t*>(L.stage[isv ? 1 : 0]) + ch;
+    const float x0 = __uint_as_float((uint32_t)rows[0] << 16);
+    float sx = 0.f;
+#pragma unroll
+    for (int t = 1; t < kBlockSize; ++t)
+      if (t < tn) sx += __uint_as_float((uint32_t)rows[t * D] << 16) - x0;
+    const float mu = x0 + sx / (float)tn;
+    const uint32_t mb = bf16_rne(mu);
+    if (isv) {
+      L.tmv[ch] = __uint_as_float(mb << 16);
+    } else {
+      reinterpret_cast<uint16_t*>(L.tmk)[ch] = (uint16_t)mb;
+      float var = 0.f;
+#pragma unroll
+      for (int t = 0; t < kBlockSize; ++t) {
+        if (t < tn) {
+          const float dl = __uint_as_float((uint32_t)rows[t * D] << 16) - mu;
+          var = fmaf(dl, dl, var);
+        }
+      }
+      tvar[ch] = var;
+    }
+  }
+  __syncthreads();
+  const size_t srow = (size_t)bg * s.max_blocks + M - 1;
+  if (tid < LPR) {
+    *reinterpret_cast<uint4*>(static_cast<KV*>(io.summ.mean_k) + srow * D + tid * 8) = L.tmk[tid];
+  } else if (tid < 2 * LPR) {
+    const float* tv = L.tmv + (tid - LPR) * 8;
+    uint4 wb;
+    wb.x = (__float_as_uint(tv[0]) >> 16) | (__float_as_uint(tv[1]) & 0xffff0000u);
+    wb.y = (__float_as_uint(tv[2]) >> 16) | (__float_as_uint(tv[3]) & 0xffff0000u);
+    wb.z = (__float_as_uint(tv[4]) >> 16) | (__float_as_uint(tv[5]) & 0xffff0000u);
+    wb.w = (__float_as_uint(tv[6]) >> 16) | (__float_as_uint(tv[7]) & 0xffff0000u);
+    *reinterpret_cast<uint4*>(static_cast<KV*>(io.summ.mean_v) + srow * D + (tid - LPR) * 8) = wb;
+  } else if (tid < 2 * LPR + 4) {
+    // group t of 32 channels: each 8-channel slice summed in order, then
+    // the four slices pairwise, as the build sums across its lanes
+    const int t = tid - 2 * LPR;
+    float sl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sl[i] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sl[i] += tvar[(4 * t + i) * 8 + e];
+    }
+    io.summ.gvar[srow * 4 + t] = ((sl[0] + sl[1]) + (sl[2] + sl[3])) / ((float)tn * (float)(D / 4));
+  } else if (tid == 2 * LPR + 4 && g == 0) {
+    io.summ.count[(size_t)b * s.max_blocks + M - 1] = tn;
+  }
+  // every store of the workgroup in L2 before the tail word
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const Coh tw(w.ctrl + kCtrlHeader + kCtrlPerPair * bg + kCtrlTail, 8, s.n_xcd > 0);
+    tw.put_u64(0, tagged(1.f, tag));
   }
 }
 
@@ -1488,6 +1534,15 @@ __global__ __launch_bounds__(NT, 2) void fused_step_kernel(Shape s_arg, StepIO i
       merge_slice<D, G>(s, io, w, bg, role, epoch, lds.m);
       CKV_MARK(role, 11);
     } else {
+      if constexpr (kApp) {
+        // the tail chunk's value workgroup appends the new token first
+        const int Lq = clamp_len(ld_uniform(io.seq_lens + bg / s.Hkv), s.max_blocks * s.bs);
+        const int Mq = (Lq + s.bs - 1) / s.bs;
+        if (Mq > 0 && ((Mq - 1) / kChunk) % s.n_val == role - s.n_chunks) {
+          append_tail<KV, D, G>(s, io, w, bg, epoch + 1u, lds.v);
+          __syncthreads();
+        }
+      }
       // value workgroup v sums chunks v, v + n_val, ... in turn
       for (int chunk = role - s.n_chunks; chunk < s.n_chunks; chunk += s.n_val) {
         val_chunk<KV, D, G, kApp>(s, io, w, bg, chunk, epoch + 1u, lds.v);

@@ -64,7 +64,8 @@ struct Shape {
 // Device pointers carved from the caller's workspace.
 struct Work {
   uint32_t* ctrl;  // [kCtrlHeader + kCtrlPerPair * B * Hkv]: error flag at 2; per (b, g):
-                   //   (spare), select arrivals, attend arrivals, fused epoch, (spare x4)
+                   //   (spare), select arrivals, attend arrivals, fused epoch, the fused
+                   //   append's tail word (64 bits, tagged; cleared by its reader), (spare x2)
   float* xs;       // [B][Hq][max_blocks]  exp(log score - chunk max of log score)
   float* cpart;    // [B][Hkv][n_chunks][G][D+4]  per chunk and head: max s_bar, sum w,
                    //   sum w (1 + var_hat/2), max log score, sum w mean_v; w = n e^{s_bar - max}
