@@ -98,7 +98,7 @@ constexpr int NW = NT / 64;                // waves per workgroup
 #define CKV_MARK(slot, i) CKV_NOTE(slot, i, 0)
 #endif
 
-constexpr int kTier1 = 32;  // k > 64: each chunk's candidates read first (plus the next key)
+constexpr int kTier1 = 32;  // k > 32: each chunk's candidates read first (plus the next key)
 constexpr int kCtrlTail = 4;  // per-pair control words 4-5: the appended tail summary is stored (tagged)
 constexpr int kPollBatch = 8;              // published words read per thread per round trip
 constexpr uint32_t kPollLimit = 1u << 20;  // re-reads per thread and wait
@@ -803,8 +803,10 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     const Coh cand(cand_half(s, w, tag) + (size_t)bg * s.n_chunks * s.kmax, (size_t)s.n_chunks * s.kmax * 8,
                    s.n_xcd > 0);
     const int k1 = min(kk, nrows);
-    const bool fast = kk <= 64;  // selections of up to one wave's width stay in registers
-    // k > 64 with room to spare in tier 1 (below): tier 2 is published only
+    // k <= 32: the one-wave selection from every chunk's top k.  Larger k
+    // (measured: from 33 to 64 blocks too) goes through the two tiers below.
+    const bool fast = kk <= 32;
+    // k > 32 with room to spare in tier 1 (below): tier 2 is published only
     // when the pair's tier 1 turns out not to hold its top k
     const bool tiered = !fast && s.n_chunks * kTier1 >= 2 * kk && s.n_chunks * (2 * kTier1 + 2) <= kFusedCand;
     // tier 2: the chunk's keys ranked kTier1 + 2 .. k1 (below k_next, its
@@ -833,7 +835,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
         if (lane < kk) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
       }
     } else {
-      // Two tiers (k > 64).  Tier 1: the chunk's kTier1 largest keys, largest
+      // Two tiers (k > 32).  Tier 1: the chunk's kTier1 largest keys, largest
       // first, in slots 0..kTier1-1, and its next largest key (the largest it
       // leaves out of tier 1) in slot kTier1, from the one-wave path's sorts.
       // Tier 2: the rest of its top k, in slots kTier1+1.., in row order.
@@ -857,7 +859,7 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
     // the pair's top-k from every chunk's candidates
     CKV_MARK(chunk, 5);
     const int n2 = s.n_chunks * kk;
-    // k > 64 with room to spare in tier 1: read tier 1 and the slots kTier1
+    // k > 32 with room to spare in tier 1: read tier 1 and the slots kTier1
     // first; the full candidates only if some chunk may hold more
     bool tier_ok = false;
     uint64_t T_tier = 0;

@@ -317,6 +317,16 @@ def test_llama_32k():
     full_check(W.make_preset("llama_32k", seed=0), fused=True)
 
 
+@pytest.mark.parametrize("preset,budget", [("llama_32k", 528), ("llama_32k", 1024), ("llama_128k", 1024)])
+def test_selection_of_33_to_64_blocks(preset, budget):
+    # 32 < k <= 64: the single launch publishes each chunk's 32 best
+    # candidates and its 33rd first, and all of its top k only if some
+    # chunk's 33rd lies above the pair's k-th; both paths against the oracle.
+    w = W.make_preset(preset, seed=5)
+    assert C.decode_step_launches(dims_of(w), budget) == 1
+    full_check(w, budget=budget)
+
+
 def test_max_context_length():
     # The widest page table the library takes (15872 blocks, 253952 tokens),
     # one token short so the last block is ragged: the single-launch step, the
