@@ -192,19 +192,26 @@ def cpu_oracle_baseline(w, runs: int = 5) -> dict:
 # ---- GPU timing --------------------------------------------------------------
 
 
-def replays_for(steps: int, want: int = 10) -> int:
-    """The largest replay count <= want that divides `steps`."""
+GRAPH_MIN_STEPS = 20  # steps per captured graph, so that its launch gap is spread thin
+
+
+def replays_for(steps: int, want: int = 10, min_per: int = GRAPH_MIN_STEPS) -> int:
+    """The largest replay count <= want that divides `steps` and leaves at
+    least min(min_per, steps) steps per replay."""
     for r in range(min(want, steps), 0, -1):
-        if steps % r == 0:
+        if steps % r == 0 and steps // r >= min(min_per, steps):
             return r
     return 1
 
 
-def timed_replays(torch, fn, steps: int, replays: int):
+def timed_replays(torch, fn, steps: int, replays: int, extra: int = 0):
     """Capture steps // replays consecutive steps fn(0), fn(1), ... into one
     HIP graph, replay it `replays` times back to back with an event between
     replays (on the capturing stream), and return (us per step over all
-    `steps`, per-replay us per step)."""
+    `steps`, per-replay us per step).  With `extra`, the per-replay figures
+    come from that many further replays of the same graph after the timed
+    ones instead (for a distribution when the timed steps fill few replays);
+    they do not enter the first figure."""
     per = steps // replays
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -220,6 +227,14 @@ def timed_replays(torch, fn, steps: int, replays: int):
     torch.cuda.synchronize()
     samples = [ev[r].elapsed_time(ev[r + 1]) * 1e3 / per for r in range(replays)]
     total = ev[0].elapsed_time(ev[replays]) * 1e3 / (per * replays)
+    if extra > 0:
+        ex = [torch.cuda.Event(enable_timing=True) for _ in range(extra + 1)]
+        ex[0].record()
+        for r in range(extra):
+            g.replay()
+            ex[r + 1].record()
+        torch.cuda.synchronize()
+        samples = [ex[r].elapsed_time(ex[r + 1]) * 1e3 / per for r in range(extra)]
     return total, samples
 
 
@@ -458,7 +473,7 @@ def batched_result(args, dev0, n_layers: int, w=None) -> dict:
     for i in range(4):
         step(i)
     torch.cuda.synchronize()
-    us, samples = timed_replays(torch, step, 40, 10)
+    us, samples = timed_replays(torch, step, 40, 2, extra=10)
     C.workspace_status(ws)
     ab = {"total": 0}
     for Lb in w.seq_lens:
@@ -613,8 +628,9 @@ def main() -> int:
     # steps / replays consecutive steps, back to back on the launch stream,
     # with an event between replays; synchronized before and after.
     replays = replays_for(args.steps)
+    extra_replays = 10 if replays < 5 else 0  # the distribution from further replays of the same graph
     t0 = time.perf_counter()
-    us_per_step, samples = timed_replays(torch, step, args.steps, replays)
+    us_per_step, samples = timed_replays(torch, step, args.steps, replays, extra=extra_replays)
     wall_s = time.perf_counter() - t0
     # every bounded wait of the timed steps ended in time (else this raises
     # and the run fails: the outputs of those steps would be unspecified)
@@ -653,7 +669,7 @@ def main() -> int:
         for i in range(3):
             dstep(i)
         torch.cuda.synchronize()
-        dense_us, dsamples = timed_replays(torch, dstep, 48, 6)
+        dense_us, dsamples = timed_replays(torch, dstep, 48, 2, extra=6)
         C.workspace_status(dws)
         dense = {"us_per_step": round(dense_us, 2), "distribution_us": distribution(dsamples),
                  "bytes": kv_all, "GBps": round(kv_all / (dense_us * 1e-6) / 1e9, 1),
@@ -668,7 +684,9 @@ def main() -> int:
                        "ckv::step_kernel x3 (score, select, attend; timed together)"),
             "algorithmic_bytes_per_launch": ab["total"], "avg_launch_us": round(avg_launch_us, 3),
             "launch_timing": f"HIP events on the launch stream around {replays} back-to-back replays of a "
-                             f"graph of {args.steps // replays} steps, {launches} launch(es) per step"}
+                             f"graph of {args.steps // replays} steps, {launches} launch(es) per step"
+                             + (f"; distribution_us from {extra_replays} further replays of the same graph"
+                                if extra_replays else "")}
     extra = {}
     if not args.no_extra and args.workload == "llama_128k":
         del layers
