@@ -824,14 +824,32 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       if (t2) cand.put_u64(chunk * s.kmax + pos, mykey);
       for (int e = max(k1, kTier1 + 1) + tid; e < kk; e += NT) cand.put_u64(chunk * s.kmax + e, 1u);
     };
-    if (fast) {
-      // each wave sorts its 64 blocks; wave 0 merges the four lists
-      const uint64_t srt = wave_sort_desc(mykey);
-      L.u.keys[tid] = srt;
+    static_assert(NW == 4, "the chunk's four sorted lists are merged in two rounds");
+    // each wave sorts its 64 blocks (L.u.keys[0..nrows) then holds the
+    // chunk's keys); waves 0 and 2 merge pairs of lists (the 64 largest of
+    // each pair, wave 2's past the chunk's keys), then wave 0 the two results.
+    // The appending instance merges the four lists one after another on wave
+    // 0 (fewer registers live at once).
+    auto chunk_top = [&]() -> uint64_t {
+      uint64_t top = wave_sort_desc(mykey);
+      L.u.keys[tid] = top;
       __syncthreads();
+      if constexpr (kApp) {
+        if (wave == 0)
+          for (int v = 1; v < NW; ++v) top = wave_merge_desc(top, L.u.keys[64 * v + 63 - lane]);
+        return top;
+      }
+      if ((wave & 1) == 0) {
+        top = wave_merge_desc(top, L.u.keys[64 * (wave + 1) + 63 - lane]);
+        if (wave == 2) L.u.keys[NT + lane] = top;
+      }
+      __syncthreads();
+      if (wave == 0) top = wave_merge_desc(top, L.u.keys[NT + 63 - lane]);
+      return top;  // wave 0: the chunk's 64 largest keys, descending
+    };
+    if (fast) {
+      const uint64_t top = chunk_top();
       if (wave == 0) {
-        uint64_t top = srt;
-        for (int v = 1; v < NW; ++v) top = wave_merge_desc(top, L.u.keys[64 * v + 63 - lane]);
         if (lane < kk) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
       }
     } else {
@@ -841,12 +859,8 @@ __device__ void ctl_chunk(const Shape& s, const StepIO& io, const Work& w, int b
       // Tier 2: the rest of its top k, in slots kTier1+1.., in row order.
       // A pair whose every slot kTier1 lies below the k-th largest tier-1 key
       // needs tier 1 only.
-      const uint64_t srt = wave_sort_desc(mykey);
-      L.u.keys[tid] = srt;  // each wave's keys sorted: rows 0..nrows-1 hold the real ones
-      __syncthreads();
+      const uint64_t top = chunk_top();
       if (wave == 0) {
-        uint64_t top = srt;
-        for (int v = 1; v < NW; ++v) top = wave_merge_desc(top, L.u.keys[64 * v + 63 - lane]);
         if (lane <= kTier1) cand.put_u64(chunk * s.kmax + lane, lane < k1 ? top : 1u);  // 1: below every real key
         const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, kTier1);
         const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), kTier1);
